@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Throughput of the DP-GRAPE private update step on one MI355X.
+
+A step is one pass of the whole path over one batch: dpg_project_clip_noise
+(P generation, projection, per-sample norms, clip, batch sum, noise) then
+dpg_adam_backproject (projected Adam, P regeneration, back-projection into W)
+over every layer of the workload. Inputs (A, dY) are synthetic, seeded, and
+resident in HBM before timing starts; W, m and v evolve in place and the step
+counter (which keys P and the noise) advances every step.
+
+Prints one JSON line: samples/s over the timed steps, the roofline position
+of the dominant kernel (per-kernel times from HIP events recorded on the
+library's stream over a second pass of the same steps), and the CPU oracle's
+rate on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mlp4]
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp4")
+    ap.add_argument("--timing-steps", type=int, default=50,
+                    help="steps of the per-kernel event pass")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def kernel_work(wl):
+    """Algorithmic bytes and flops of each kernel kind for one step of `wl`.
+
+    Bytes count each input the kernel must read once and each output it must
+    write once (es = bytes per A/dY element); flops count the multiply-adds of
+    its matrix-core contraction (2 per MAC)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    B, T, r = wl.B, wl.T, wl.r
+    w = {k: [0.0, 0.0] for k in ("gen_p", "proj", "norm", "scale", "sum",
+                                 "fin", "adam", "gen_pt", "back")}
+    for L in wl.layers:
+        di, do = L.d_in, L.d_out
+        w["gen_p"][0] += r * di * es
+        w["proj"][0] += B * T * di * es + r * di * es + B * T * r * es
+        w["proj"][1] += 2.0 * B * T * di * r
+        w["norm"][0] += B * T * do * es + B * T * r * es
+        w["norm"][1] += 2.0 * B * T * r * do
+        w["sum"][0] += B * T * do * es + B * T * r * es
+        w["sum"][1] += 2.0 * B * T * r * do
+        w["fin"][0] += 2 * r * do * 4
+        w["adam"][0] += r * do * (5 * 4 + es)
+        w["gen_pt"][0] += r * di * es
+        w["back"][0] += 8 * di * do + (di + do) * r * es
+        w["back"][1] += 2.0 * di * r * do
+    w["scale"][0] += B * 4
+    return w
+
+
+def cpu_baseline(wl, host, state, reps):
+    """The float64 oracle on the full step of the same workload."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    orc = [{"A": W.as_float64(wl, a), "dY": W.as_float64(wl, d),
+            "layer_id": L.layer_id} for (a, d), L in zip(host, wl.layers)]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        res = oracle.project_clip_noise(orc, wl.r, wl.clip_C, wl.sigma,
+                                        wl.seed, wl.step, wl.proj_step)
+        params = [{"W": s[0], "m": s[1], "v": s[2], "G_priv": g,
+                   "layer_id": L.layer_id}
+                  for s, g, L in zip(state, res["G_priv"], wl.layers)]
+        oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2,
+                                wl.eps, wl.seed, wl.step, wl.proj_step)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(wl.B / t, 3), "unit": "samples/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"full step of {wl.name} ({wl.B} samples, "
+                      f"{len(wl.layers)} layers), float64 numpy, median of "
+                      f"{reps} runs of {[round(x, 2) for x in times]} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs the DP-GRAPE step on one GPU; --gpus {args.gpus} "
+              "is not supported by this build (no multi-GPU path).",
+              file=sys.stderr)
+        sys.exit(2)
+    for k in ("RANK", "WORLD_SIZE"):
+        if os.environ.get(k) not in (None, "0", "1") and k == "WORLD_SIZE":
+            print("bench.py is single-GPU only", file=sys.stderr)
+            sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dp_grape_projection_amd as dpg
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dpg.load_library()
+    wl = W.workload(args.workload)
+    dev = torch.device("cuda:0")
+
+    t_gen = time.perf_counter()
+    host = [W.layer_inputs(wl, L) for L in wl.layers]
+    state = [W.initial_state(wl, L) for L in wl.layers]
+
+    def to_dev(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    A = [to_dev(a) for a, _ in host]
+    dY = [to_dev(d) for _, d in host]
+    Wd = [torch.from_numpy(s[0].copy()).to(dev) for s in state]
+    md = [torch.zeros_like(torch.from_numpy(s[1])).to(dev) for s in state]
+    vd = [torch.zeros_like(torch.from_numpy(s[2])).to(dev) for s in state]
+    prep = dpg.PreparedStep(A, dY, Wd, md, vd, wl.r, wl.clip_C, wl.sigma,
+                            wl.seed, wl.lr, wl.beta1, wl.beta2, wl.eps,
+                            layer_ids=[L.layer_id for L in wl.layers])
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: inputs ready in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        prep.run(step)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step += 1
+        prep.run(step)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    value = wl.B * args.steps / wall
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step "
+          f"(events {ev_ms * 1e3 / args.steps:.1f} us/step)", file=sys.stderr,
+          flush=True)
+
+    # Per-kernel times: events around each launch on the library's stream.
+    dpg.timing_read(reset=True)
+    dpg.timing_enable(True)
+    for _ in range(args.timing_steps):
+        step += 1
+        prep.run(step)
+    torch.cuda.synchronize()
+    times = dpg.timing_read(reset=True)
+    dpg.timing_enable(False)
+    work = kernel_work(wl)
+    peak_flops = BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    kernels = {}
+    for name, (ms, n) in times.items():
+        if n == 0:
+            continue
+        per_step_launches = n / args.timing_steps
+        avg_us = ms * 1e3 / n
+        byt, flo = work[name]
+        # one step's work is split evenly over that step's launches
+        byt_l, flo_l = byt / per_step_launches, flo / per_step_launches
+        kernels[name] = {
+            "avg_us": round(avg_us, 2), "launches_per_step": per_step_launches,
+            "us_per_step": round(avg_us * per_step_launches, 2),
+            "GB/s": round(byt_l / (avg_us * 1e-6) / 1e9, 1),
+            "TFLOP/s": round(flo_l / (avg_us * 1e-6) / 1e12, 2)}
+    dom = max(kernels, key=lambda k: kernels[k]["us_per_step"])
+    dk = kernels[dom]
+    roof = {"kernel": dom, "bound": "hbm", "achieved": dk["GB/s"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "mfma_TFLOP/s": dk["TFLOP/s"],
+            "mfma_frac": round(dk["TFLOP/s"] / peak_flops, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, host, state, args.cpu_reps)
+
+    layers = "->".join([str(wl.layers[0].d_in)] + [str(L.d_out) for L in wl.layers]) \
+        if all(a.d_out == b.d_in for a, b in zip(wl.layers, wl.layers[1:])) \
+        else f"{len(wl.layers)} layers"
+    out = {
+        "metric": "DP-GRAPE step samples/sec at 1 GPU; MFMA % of bf16 peak, HBM GB/s",
+        "value": round(value, 1), "unit": "samples/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded Gaussian A, dY; Gaussian W)",
+        "config": {"workload": wl.name, "layers": layers, "B": wl.B,
+                   "T": wl.T, "r": wl.r, "clip_C": wl.clip_C,
+                   "sigma": wl.sigma, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,11 @@
+"""DP-GRAPE private update step on one AMD MI355X (gfx950).
+
+The compute lives in libdpg.so (C ABI in include/dpg.h, HIP kernels in
+csrc/); this package is its thin Python binding.
+"""
+from .binding import (  # noqa: F401
+    DPG_BF16, DPG_FP32, DpgError, EXPORTED, LayerGrad, LayerParam, PreparedStep,
+    adam_workspace_size, dpg_adam_backproject, dpg_philox_normals,
+    dpg_project_clip_noise, library_path, load_library,
+    project_workspace_size, timing_enable, timing_read, version,
+)

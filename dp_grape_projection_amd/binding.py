@@ -1,0 +1,368 @@
+"""ctypes binding of libdpg.so (include/dpg.h): argument marshalling only.
+
+Every step of the DP-GRAPE update runs in the library's HIP kernels; this
+module turns torch tensors into device pointers and the current HIP stream,
+and allocates outputs and workspaces with torch when the caller does not pass
+them. It never computes any part of the method itself, and it raises when the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence
+
+import torch  # loaded first: libdpg.so then shares torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdpg.so")
+
+DPG_OK = 0
+DPG_ERR_INVALID_ARG = 1
+DPG_ERR_WORKSPACE = 2
+DPG_ERR_UNSUPPORTED = 3
+DPG_ERR_HIP = 4
+DPG_FP32 = 0
+DPG_BF16 = 1
+
+EXPORTED = (
+    "dpg_project_workspace_size", "dpg_project_clip_noise",
+    "dpg_adam_workspace_size", "dpg_adam_backproject", "dpg_philox_normals",
+    "dpg_status_string", "dpg_last_error", "dpg_version",
+    "dpg_timing_enable", "dpg_timing_read", "dpg_kernel_name",
+)
+N_KERNEL_KINDS = 9
+
+
+class DpgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class LayerGrad(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64),
+                ("layer_id", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("A", ctypes.c_void_p), ("dY", ctypes.c_void_p),
+                ("G_priv", ctypes.c_void_p)]
+
+
+class LayerParam(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64),
+                ("layer_id", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("G_priv", ctypes.c_void_p), ("W", ctypes.c_void_p),
+                ("m", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libdpg.so (once). Raises FileNotFoundError when it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} is missing: build it with `python -m dp_grape_projection_amd.build`")
+    lib = ctypes.CDLL(p)
+    i32, i64, u32, u64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                          ctypes.c_uint64)
+    f32, vp, sz = ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    lib.dpg_project_workspace_size.argtypes = [
+        ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, ctypes.POINTER(sz)]
+    lib.dpg_project_clip_noise.argtypes = [
+        ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, f32, f32, u64,
+        u64, u64, vp, vp, sz, vp]
+    lib.dpg_adam_workspace_size.argtypes = [
+        ctypes.POINTER(LayerParam), i32, i32, i32, ctypes.POINTER(sz)]
+    lib.dpg_adam_backproject.argtypes = [
+        ctypes.POINTER(LayerParam), i32, i32, i32, f32, f32, f32, f32, u64,
+        u64, u64, vp, sz, vp]
+    lib.dpg_philox_normals.argtypes = [u64, u32, u32, u32, u64, u64, vp, vp, vp]
+    for name in EXPORTED:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.dpg_status_string.restype = ctypes.c_char_p
+    lib.dpg_status_string.argtypes = [ctypes.c_int]
+    lib.dpg_last_error.restype = ctypes.c_char_p
+    lib.dpg_last_error.argtypes = []
+    lib.dpg_timing_enable.argtypes = [ctypes.c_int]
+    lib.dpg_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64), i32,
+                                    ctypes.c_int]
+    lib.dpg_kernel_name.restype = ctypes.c_char_p
+    lib.dpg_kernel_name.argtypes = [ctypes.c_int]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != DPG_OK:
+        msg = lib.dpg_last_error().decode() or lib.dpg_status_string(status).decode()
+        raise DpgError(status, msg)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return DPG_BF16
+    if t == torch.float32:
+        return DPG_FP32
+    raise TypeError(f"A/dY must be bfloat16 or float32, got {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if workspace is not None:
+        _require(workspace, "workspace", torch.uint8)
+        return workspace, workspace.numel()
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+
+
+def project_workspace_size(shapes: Sequence, B: int, T: int, r: int,
+                           dtype: torch.dtype,
+                           layer_ids: Optional[Sequence[int]] = None) -> int:
+    """Workspace bytes dpg_project_clip_noise needs; shapes = [(d_in, d_out)]."""
+    lib = load_library()
+    n = len(shapes)
+    ids = list(range(n)) if layer_ids is None else list(layer_ids)
+    arr = (LayerGrad * n)()
+    for i, ((di, do), lid) in enumerate(zip(shapes, ids)):
+        arr[i].d_in, arr[i].d_out, arr[i].layer_id = int(di), int(do), int(lid)
+    out = ctypes.c_size_t(0)
+    _check(lib, lib.dpg_project_workspace_size(arr, n, int(B), int(T), int(r),
+                                               _dtype_code(dtype),
+                                               ctypes.byref(out)))
+    return out.value
+
+
+def adam_workspace_size(shapes: Sequence, r: int, dtype: torch.dtype,
+                        layer_ids: Optional[Sequence[int]] = None) -> int:
+    lib = load_library()
+    n = len(shapes)
+    ids = list(range(n)) if layer_ids is None else list(layer_ids)
+    arr = (LayerParam * n)()
+    for i, ((di, do), lid) in enumerate(zip(shapes, ids)):
+        arr[i].d_in, arr[i].d_out, arr[i].layer_id = int(di), int(do), int(lid)
+    out = ctypes.c_size_t(0)
+    _check(lib, lib.dpg_adam_workspace_size(arr, n, int(r), _dtype_code(dtype),
+                                            ctypes.byref(out)))
+    return out.value
+
+
+def dpg_project_clip_noise(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
+                           r: int, clip_C: float, sigma: float, seed: int,
+                           step: int, proj_step: Optional[int] = None,
+                           layer_ids: Optional[Sequence[int]] = None,
+                           G_priv: Optional[List[torch.Tensor]] = None,
+                           sample_norms: Optional[torch.Tensor] = None,
+                           return_norms: bool = True,
+                           workspace: Optional[torch.Tensor] = None,
+                           stream=None):
+    """Projection, global per-sample clip, batch sum and noise (libdpg).
+
+    A[l]: [B, T, d_in_l], dY[l]: [B, T, d_out_l] (bf16 or fp32, on the GPU).
+    Returns (G_priv list of [r, d_out_l] fp32, sample norms [B] or None)."""
+    lib = load_library()
+    n = len(A)
+    if n < 1 or len(dY) != n:
+        raise ValueError("A and dY must be non-empty lists of equal length")
+    dt = A[0].dtype
+    B, T = int(A[0].shape[0]), int(A[0].shape[1])
+    ids = list(range(n)) if layer_ids is None else [int(x) for x in layer_ids]
+    proj_step = step if proj_step is None else proj_step
+    dev = A[0].device
+    if G_priv is None:
+        G_priv = [torch.empty((r, int(d.shape[2])), dtype=torch.float32,
+                              device=dev) for d in dY]
+    if sample_norms is None and return_norms:
+        sample_norms = torch.empty(B, dtype=torch.float32, device=dev)
+    arr = (LayerGrad * n)()
+    for i in range(n):
+        _require(A[i], f"A[{i}]", dt)
+        _require(dY[i], f"dY[{i}]", dt)
+        if A[i].dim() != 3 or dY[i].dim() != 3 or \
+                tuple(A[i].shape[:2]) != (B, T) or tuple(dY[i].shape[:2]) != (B, T):
+            raise ValueError(f"layer {i}: A and dY must be [B, T, d] with common B, T")
+        d_in, d_out = int(A[i].shape[2]), int(dY[i].shape[2])
+        _require(G_priv[i], f"G_priv[{i}]", torch.float32, (r, d_out))
+        arr[i].d_in, arr[i].d_out, arr[i].layer_id = d_in, d_out, ids[i]
+        arr[i].A, arr[i].dY, arr[i].G_priv = _ptr(A[i]), _ptr(dY[i]), _ptr(G_priv[i])
+    if sample_norms is not None:
+        _require(sample_norms, "sample_norms", torch.float32, (B,))
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.dpg_project_workspace_size(arr, n, B, T, int(r),
+                                               _dtype_code(dt), ctypes.byref(need)))
+    ws, ws_bytes = _workspace(need.value, dev, workspace)
+    _check(lib, lib.dpg_project_clip_noise(
+        arr, n, B, T, int(r), _dtype_code(dt), float(clip_C), float(sigma),
+        int(seed), int(step), int(proj_step), _ptr(sample_norms),
+        ws.data_ptr(), ws_bytes, _stream_handle(stream)))
+    return G_priv, sample_norms
+
+
+def dpg_adam_backproject(G_priv: Sequence[torch.Tensor], W: Sequence[torch.Tensor],
+                         m: Sequence[torch.Tensor], v: Sequence[torch.Tensor],
+                         r: int, lr: float, beta1: float, beta2: float,
+                         eps: float, seed: int, step: int,
+                         proj_step: Optional[int] = None,
+                         layer_ids: Optional[Sequence[int]] = None,
+                         dtype: torch.dtype = torch.bfloat16,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """Projected Adam and back-projection W -= lr P^T U, in place (libdpg).
+
+    dtype is the operand precision of P^T U (bf16 or fp32)."""
+    lib = load_library()
+    n = len(W)
+    ids = list(range(n)) if layer_ids is None else [int(x) for x in layer_ids]
+    proj_step = step if proj_step is None else proj_step
+    arr = (LayerParam * n)()
+    for i in range(n):
+        _require(W[i], f"W[{i}]", torch.float32)
+        if W[i].dim() != 2:
+            raise ValueError(f"W[{i}] must be [d_in, d_out]")
+        d_in, d_out = int(W[i].shape[0]), int(W[i].shape[1])
+        for name, t in (("G_priv", G_priv[i]), ("m", m[i]), ("v", v[i])):
+            _require(t, f"{name}[{i}]", torch.float32, (r, d_out))
+        arr[i].d_in, arr[i].d_out, arr[i].layer_id = d_in, d_out, ids[i]
+        arr[i].G_priv, arr[i].W = _ptr(G_priv[i]), _ptr(W[i])
+        arr[i].m, arr[i].v = _ptr(m[i]), _ptr(v[i])
+    code = _dtype_code(dtype)
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.dpg_adam_workspace_size(arr, n, int(r), code, ctypes.byref(need)))
+    ws, ws_bytes = _workspace(need.value, W[0].device, workspace)
+    _check(lib, lib.dpg_adam_backproject(
+        arr, n, int(r), code, float(lr), float(beta1), float(beta2), float(eps),
+        int(seed), int(step), int(proj_step), ws.data_ptr(), ws_bytes,
+        _stream_handle(stream)))
+    return W, m, v
+
+
+def dpg_philox_normals(seed: int, layer_id: int, step_word: int, tag: int,
+                       start: int, n: int, device="cuda", words: bool = False,
+                       stream=None):
+    """The library's random stream z(e), e in [start, start+n) (and raw words)."""
+    lib = load_library()
+    z = torch.empty(n, dtype=torch.float32, device=device)
+    w = None
+    if words and n > 0:
+        n_ctr = ((start + n - 1) >> 2) - (start >> 2) + 1
+        w = torch.empty(4 * n_ctr, dtype=torch.int32, device=device)
+    _check(lib, lib.dpg_philox_normals(int(seed), int(layer_id), int(step_word),
+                                       int(tag), int(start), int(n), _ptr(z),
+                                       _ptr(w), _stream_handle(stream)))
+    return (z, w) if words else z
+
+
+class PreparedStep:
+    """One DP-GRAPE step (dpg_project_clip_noise then dpg_adam_backproject)
+    with its layer tables and workspaces marshalled once, for callers that
+    repeat the step on the same buffers (a training loop, the bench).
+
+    run(step) enqueues both calls on the current stream with
+    step = proj_step = `step`."""
+
+    def __init__(self, A, dY, W, m, v, r, clip_C, sigma, seed, lr, beta1,
+                 beta2, eps, layer_ids=None, G_priv=None, sample_norms=None):
+        self.lib = load_library()
+        n = len(A)
+        dt = A[0].dtype
+        self.dtype_code = _dtype_code(dt)
+        self.B, self.T = int(A[0].shape[0]), int(A[0].shape[1])
+        ids = list(range(n)) if layer_ids is None else [int(x) for x in layer_ids]
+        dev = A[0].device
+        self.G_priv = G_priv or [torch.empty((r, int(d.shape[2])),
+                                             dtype=torch.float32, device=dev)
+                                 for d in dY]
+        self.sample_norms = (torch.empty(self.B, dtype=torch.float32, device=dev)
+                             if sample_norms is None else sample_norms)
+        self.grads = (LayerGrad * n)()
+        self.params = (LayerParam * n)()
+        for i in range(n):
+            _require(A[i], f"A[{i}]", dt)
+            _require(dY[i], f"dY[{i}]", dt)
+            d_in, d_out = int(A[i].shape[2]), int(dY[i].shape[2])
+            _require(W[i], f"W[{i}]", torch.float32, (d_in, d_out))
+            for name, t in (("G_priv", self.G_priv[i]), ("m", m[i]), ("v", v[i])):
+                _require(t, f"{name}[{i}]", torch.float32, (r, d_out))
+            g, p = self.grads[i], self.params[i]
+            g.d_in = p.d_in = d_in
+            g.d_out = p.d_out = d_out
+            g.layer_id = p.layer_id = ids[i]
+            g.A, g.dY, g.G_priv = A[i].data_ptr(), dY[i].data_ptr(), \
+                self.G_priv[i].data_ptr()
+            p.G_priv, p.W = self.G_priv[i].data_ptr(), W[i].data_ptr()
+            p.m, p.v = m[i].data_ptr(), v[i].data_ptr()
+        self.n = n
+        self.r = int(r)
+        self.hyper = (float(clip_C), float(sigma), int(seed), float(lr),
+                      float(beta1), float(beta2), float(eps))
+        need1, need2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(self.lib, self.lib.dpg_project_workspace_size(
+            self.grads, n, self.B, self.T, self.r, self.dtype_code,
+            ctypes.byref(need1)))
+        _check(self.lib, self.lib.dpg_adam_workspace_size(
+            self.params, n, self.r, self.dtype_code, ctypes.byref(need2)))
+        self.ws1, self.ws1_bytes = _workspace(need1.value, dev, None)
+        self.ws2, self.ws2_bytes = _workspace(need2.value, dev, None)
+        self._keep = (A, dY, W, m, v)
+
+    def run(self, step: int, stream=None) -> None:
+        C, sigma, seed, lr, b1, b2, eps = self.hyper
+        h = _stream_handle(stream)
+        lib = self.lib
+        _check(lib, lib.dpg_project_clip_noise(
+            self.grads, self.n, self.B, self.T, self.r, self.dtype_code, C,
+            sigma, seed, step, step, self.sample_norms.data_ptr(),
+            self.ws1.data_ptr(), self.ws1_bytes, h))
+        _check(lib, lib.dpg_adam_backproject(
+            self.params, self.n, self.r, self.dtype_code, lr, b1, b2, eps,
+            seed, step, step, self.ws2.data_ptr(), self.ws2_bytes, h))
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every kernel launch of the two step calls with HIP events."""
+    lib = load_library()
+    _check(lib, lib.dpg_timing_enable(1 if on else 0))
+
+
+def timing_read(reset: bool = True) -> dict:
+    """{kernel name: (total ms, launches)} since the last reset."""
+    lib = load_library()
+    ms = (ctypes.c_double * N_KERNEL_KINDS)()
+    cnt = (ctypes.c_int64 * N_KERNEL_KINDS)()
+    _check(lib, lib.dpg_timing_read(ms, cnt, N_KERNEL_KINDS, 1 if reset else 0))
+    return {lib.dpg_kernel_name(k).decode(): (ms[k], cnt[k])
+            for k in range(N_KERNEL_KINDS)}
+
+
+def version() -> int:
+    return load_library().dpg_version()

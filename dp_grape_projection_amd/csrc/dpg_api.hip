@@ -1,0 +1,644 @@
+// Host side of the C ABI declared in include/dpg.h: argument validation,
+// workspace planning and launch sequencing on the caller's stream. Nothing
+// is allocated here and no state survives a call (apart from the calling
+// thread's last error message).
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dpg.h"
+#include "dpg_internal.hpp"
+
+using namespace dpg;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = std::getenv("DPG_DEBUG_SYNC");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+// ---- kernel-timing diagnostics (off unless dpg_timing_enable(1))
+enum Kind { K_GEN_P, K_PROJ, K_NORM, K_SCALE, K_SUM, K_FIN, K_ADAM, K_GEN_PT,
+            K_BACK, K_COUNT };
+static_assert(K_COUNT == DPG_N_KERNEL_KINDS, "kernel kinds");
+const char* const kKindName[K_COUNT] = {"gen_p", "proj", "norm", "scale", "sum",
+                                        "fin", "adam", "gen_pt", "back"};
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimedLaunch> g_pending;
+double g_total_ms[K_COUNT] = {};
+int64_t g_launches[K_COUNT] = {};
+
+// Brackets one launch with events on its stream when timing is enabled.
+struct LaunchTimer {
+  int kind;
+  hipStream_t s;
+  hipEvent_t start = nullptr;
+  LaunchTimer(int k, hipStream_t st) : kind(k), s(st) {
+    std::lock_guard<std::mutex> g(g_timing_mu);
+    if (!g_timing_on) return;
+    if (hipEventCreate(&start) != hipSuccess) { start = nullptr; return; }
+    hipEventRecord(start, s);
+  }
+  void done() {
+    if (!start) return;
+    hipEvent_t stop;
+    if (hipEventCreate(&stop) != hipSuccess) { hipEventDestroy(start); return; }
+    hipEventRecord(stop, s);
+    std::lock_guard<std::mutex> g(g_timing_mu);
+    g_pending.push_back({kind, start, stop});
+    start = nullptr;
+  }
+};
+
+// Checks a launch; with DPG_DEBUG_SYNC=1 also waits for it to finish.
+int check(hipError_t e, const char* what, hipStream_t s) {
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(s);
+  if (e != hipSuccess)
+    return fail(DPG_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return DPG_OK;
+}
+
+// A timed launch: `fn` enqueues one kernel and returns its hipError_t.
+template <class F>
+int timed(int kind, hipStream_t s, F fn) {
+  LaunchTimer t(kind, s);
+  const hipError_t e = fn();
+  t.done();
+  return check(e, kKindName[kind], s);
+}
+
+constexpr size_t kAlign = 256;
+constexpr uint64_t kMaxU32 = 0xFFFFFFFFull;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int32_t dtype) { return dtype == DPG_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t dtype) { return dtype == DPG_FP32 || dtype == DPG_BF16; }
+
+// Shape checks shared by both calls. Limits keep every kernel index in range:
+// r*d fits the 32-bit Philox element counter, tile counts fit int32.
+int check_layer_shape(int64_t d_in, int64_t d_out, int32_t r, int idx) {
+  const std::string at = " (layer index " + std::to_string(idx) + ")";
+  if (d_in < 1 || d_out < 1)
+    return fail(DPG_ERR_INVALID_ARG, "d_in and d_out must be >= 1" + at);
+  if (d_in > (1 << 30) || d_out > (1 << 30))
+    return fail(DPG_ERR_INVALID_ARG, "d_in and d_out must be <= 2^30" + at);
+  if (static_cast<uint64_t>(r) * d_in > kMaxU32 - 8 ||
+      static_cast<uint64_t>(r) * d_out > kMaxU32 - 8)
+    return fail(DPG_ERR_INVALID_ARG, "r*d_in and r*d_out must be < 2^32" + at);
+  return DPG_OK;
+}
+
+template <class L>
+int check_unique_ids(const L* layers, int32_t n) {
+  std::vector<uint32_t> ids(n);
+  for (int i = 0; i < n; ++i) ids[i] = layers[i].layer_id;
+  std::sort(ids.begin(), ids.end());
+  for (int i = 1; i < n; ++i)
+    if (ids[i] == ids[i - 1])
+      return fail(DPG_ERR_INVALID_ARG,
+                  "duplicate layer_id " + std::to_string(ids[i]));
+  return DPG_OK;
+}
+
+// ------------------------------------------------ projection call planning --
+
+struct ProjPlan {
+  int64_t ldt = 0;             // row stride of Xt (T rounded up to 8)
+  std::vector<int64_t> ldp;    // row stride of P per layer
+  std::vector<size_t> off_P, off_Xt, off_part;
+  std::vector<int32_t> m_tiles_proj, n_tiles_proj, m_tiles_s, n_tiles_s, slot0;
+  int32_t n_slots = 0;
+  int32_t groups = 1, per_group = 1;
+  size_t off_norm = 0, off_scales = 0, total = 0;
+};
+
+int validate_proj_shapes(const dpg_layer_grad* layers, int32_t n_layers,
+                         int64_t B, int64_t T, int32_t r, int32_t dtype) {
+  if (!layers) return fail(DPG_ERR_INVALID_ARG, "layers is NULL");
+  if (n_layers < 1 || n_layers > (1 << 20))
+    return fail(DPG_ERR_INVALID_ARG, "n_layers must be in [1, 2^20]");
+  if (B < 1 || T < 1 || r < 1)
+    return fail(DPG_ERR_INVALID_ARG, "B, T and r must be >= 1");
+  if (B * T > (1ll << 30))
+    return fail(DPG_ERR_INVALID_ARG, "B*T must be <= 2^30");
+  if (!valid_dtype(dtype)) return fail(DPG_ERR_INVALID_ARG, "unknown dtype");
+  for (int i = 0; i < n_layers; ++i) {
+    const int st = check_layer_shape(layers[i].d_in, layers[i].d_out, r, i);
+    if (st) return st;
+    if (layers[i].reserved != 0)
+      return fail(DPG_ERR_INVALID_ARG, "reserved field must be 0");
+    if (B * T * std::max(layers[i].d_in, layers[i].d_out) > (1ll << 46))
+      return fail(DPG_ERR_INVALID_ARG, "layer too large");
+  }
+  return check_unique_ids(layers, n_layers);
+}
+
+ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
+                   int64_t T, int32_t r, int32_t dtype) {
+  ProjPlan p;
+  const size_t es = elem_size(dtype);
+  p.ldt = round_up(T, 8);
+  size_t off = 0;
+  int64_t tiles_sum = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const int64_t ldp = round_up(layers[l].d_in, 8);
+    p.ldp.push_back(ldp);
+    p.off_P.push_back(off);
+    off = align_up(off + static_cast<size_t>(r) * ldp * es);
+    p.off_Xt.push_back(off);
+    off = align_up(off + static_cast<size_t>(B) * r * p.ldt * es);
+    p.m_tiles_proj.push_back(static_cast<int32_t>(ceil_div(r, kProjBM)));
+    p.n_tiles_proj.push_back(static_cast<int32_t>(ceil_div(B * T, kProjBN)));
+    const int32_t mt = static_cast<int32_t>(ceil_div(r, kSampBM));
+    const int32_t nt = static_cast<int32_t>(ceil_div(layers[l].d_out, kSampBN));
+    p.m_tiles_s.push_back(mt);
+    p.n_tiles_s.push_back(nt);
+    p.slot0.push_back(p.n_slots);
+    p.n_slots += mt * nt;
+    tiles_sum += static_cast<int64_t>(mt) * nt;
+  }
+  // Sample groups of the second (sum) pass: enough blocks to cover the chip,
+  // each group adds one fp32 partial of G_priv.
+  int64_t groups = std::max<int64_t>(1, ceil_div(512, tiles_sum));
+  groups = std::min<int64_t>(groups, B);
+  p.per_group = static_cast<int32_t>(ceil_div(B, groups));
+  p.groups = static_cast<int32_t>(ceil_div(B, p.per_group));
+  for (int l = 0; l < n_layers; ++l) {
+    p.off_part.push_back(off);
+    off = align_up(off + static_cast<size_t>(p.groups) * r * layers[l].d_out * 4);
+  }
+  p.off_norm = off;
+  off = align_up(off + static_cast<size_t>(B) * p.n_slots * 4);
+  p.off_scales = off;
+  off = align_up(off + static_cast<size_t>(B) * 4);
+  p.total = off;
+  return p;
+}
+
+// ---------------------------------------------------- update call planning --
+
+struct AdamPlan {
+  int64_t ldr = 0;
+  std::vector<size_t> off_Pt, off_Ut;
+  size_t total = 0;
+};
+
+int validate_adam_shapes(const dpg_layer_param* params, int32_t n_layers,
+                         int32_t r, int32_t dtype) {
+  if (!params) return fail(DPG_ERR_INVALID_ARG, "params is NULL");
+  if (n_layers < 1 || n_layers > (1 << 20))
+    return fail(DPG_ERR_INVALID_ARG, "n_layers must be in [1, 2^20]");
+  if (r < 1) return fail(DPG_ERR_INVALID_ARG, "r must be >= 1");
+  if (!valid_dtype(dtype)) return fail(DPG_ERR_INVALID_ARG, "unknown dtype");
+  for (int i = 0; i < n_layers; ++i) {
+    const int st = check_layer_shape(params[i].d_in, params[i].d_out, r, i);
+    if (st) return st;
+    if (params[i].reserved != 0)
+      return fail(DPG_ERR_INVALID_ARG, "reserved field must be 0");
+  }
+  return check_unique_ids(params, n_layers);
+}
+
+AdamPlan plan_adam(const dpg_layer_param* params, int32_t n_layers, int32_t r,
+                   int32_t dtype) {
+  AdamPlan p;
+  const size_t es = elem_size(dtype);
+  p.ldr = round_up(r, 8);
+  size_t off = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    p.off_Pt.push_back(off);
+    off = align_up(off + static_cast<size_t>(params[l].d_in) * p.ldr * es);
+    p.off_Ut.push_back(off);
+    off = align_up(off + static_cast<size_t>(params[l].d_out) * p.ldr * es);
+  }
+  p.total = off;
+  return p;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+  if (need > 0 && !ws) return fail(DPG_ERR_WORKSPACE, "workspace is NULL");
+  if (have < need)
+    return fail(DPG_ERR_WORKSPACE, "workspace too small: need " +
+                                       std::to_string(need) + " bytes, got " +
+                                       std::to_string(have));
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return fail(DPG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return DPG_OK;
+}
+
+int check_seed_steps(uint64_t step, uint64_t proj_step) {
+  if (step < 1 || step > kMaxU32)
+    return fail(DPG_ERR_INVALID_ARG, "step must be in [1, 2^32)");
+  if (proj_step > kMaxU32)
+    return fail(DPG_ERR_INVALID_ARG, "proj_step must be < 2^32");
+  return DPG_OK;
+}
+
+bool aligned(const void* p, size_t a) {
+  return reinterpret_cast<uintptr_t>(p) % a == 0;
+}
+
+// Enqueue P generation for layers [l0, l1).
+template <class GetDin, class GetOut>
+int enqueue_gen_p(int l0, int l1, GetDin din, GetOut out_ld, uint32_t (*id)(int, const void*),
+                  const void* layers, int32_t r, uint64_t seed, uint32_t step_word,
+                  bool bf16, bool transposed, hipStream_t s) {
+  GenPArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.r = r;
+  a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(r)));
+  a.k0 = static_cast<uint32_t>(seed);
+  a.k1 = static_cast<uint32_t>(seed >> 32);
+  a.step_word = step_word;
+  int blocks = 0;
+  for (int l = l0; l < l1; ++l) {
+    GenPLayer& L = a.L[l - l0];
+    void* o;
+    int64_t ld;
+    out_ld(l, &o, &ld);
+    L.out = o;
+    L.ld = static_cast<int32_t>(ld);
+    L.d_in = static_cast<int32_t>(din(l));
+    L.layer_id = id(l, layers);
+    const uint64_t n = static_cast<uint64_t>(r) * L.d_in;
+    L.n_ctr = static_cast<int32_t>((n + 3) / 4);
+    L.block0 = blocks;
+    blocks += static_cast<int>(ceil_div(L.n_ctr, kThreads));
+  }
+  a.n_layers = l1 - l0;
+  return timed(transposed ? K_GEN_PT : K_GEN_P, s,
+               [&] { return launch_gen_p(a, blocks, bf16, transposed, s); });
+}
+
+uint32_t grad_id(int l, const void* p) {
+  return static_cast<const dpg_layer_grad*>(p)[l].layer_id;
+}
+uint32_t param_id(int l, const void* p) {
+  return static_cast<const dpg_layer_param*>(p)[l].layer_id;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dpg_version(void) { return 10000; }
+
+const char* dpg_status_string(int status) {
+  switch (status) {
+    case DPG_OK: return "DPG_OK";
+    case DPG_ERR_INVALID_ARG: return "DPG_ERR_INVALID_ARG: invalid argument";
+    case DPG_ERR_WORKSPACE: return "DPG_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case DPG_ERR_UNSUPPORTED: return "DPG_ERR_UNSUPPORTED: unsupported configuration";
+    case DPG_ERR_HIP: return "DPG_ERR_HIP: HIP runtime error";
+    default: return "unknown dpg status";
+  }
+}
+
+const char* dpg_last_error(void) { return g_last_error.c_str(); }
+
+int dpg_project_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
+                               int64_t B, int64_t T, int32_t r, int32_t dtype,
+                               size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
+  if (st) return st;
+  *bytes = plan_proj(layers, n_layers, B, T, r, dtype).total;
+  return DPG_OK;
+}
+
+int dpg_adam_workspace_size(const dpg_layer_param* params, int32_t n_layers,
+                            int32_t r, int32_t dtype, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = validate_adam_shapes(params, n_layers, r, dtype);
+  if (st) return st;
+  *bytes = plan_adam(params, n_layers, r, dtype).total;
+  return DPG_OK;
+}
+
+int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
+                           int64_t B, int64_t T, int32_t r, int32_t dtype,
+                           float clip_C, float sigma, uint64_t seed,
+                           uint64_t step, uint64_t proj_step,
+                           float* sample_norms, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
+  if (st) return st;
+  for (int i = 0; i < n_layers; ++i)
+    if (!layers[i].A || !layers[i].dY || !layers[i].G_priv)
+      return fail(DPG_ERR_INVALID_ARG,
+                  "NULL data pointer in layer index " + std::to_string(i));
+  if (!(clip_C > 0.0f))
+    return fail(DPG_ERR_INVALID_ARG, "clip_C must be > 0");
+  if (!(sigma >= 0.0f) || std::isinf(sigma))
+    return fail(DPG_ERR_INVALID_ARG, "sigma must be finite and >= 0");
+  if (std::isinf(clip_C) && sigma != 0.0f)
+    return fail(DPG_ERR_INVALID_ARG, "sigma must be 0 when clip_C is infinite");
+  if ((st = check_seed_steps(step, proj_step))) return st;
+  const ProjPlan p = plan_proj(layers, n_layers, B, T, r, dtype);
+  if ((st = check_workspace(workspace, workspace_bytes, p.total))) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const bool bf16 = dtype == DPG_BF16;
+  const size_t es = elem_size(dtype);
+  const int vec_elems = static_cast<int>(16 / es);
+  float* norm_part = reinterpret_cast<float*>(ws + p.off_norm);
+  float* scales = reinterpret_cast<float*>(ws + p.off_scales);
+
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int l1 = std::min(n_layers, l0 + kMaxLayers);
+    // 1. P_l, row-major [r][ldp]
+    st = enqueue_gen_p(
+        l0, l1, [&](int l) { return layers[l].d_in; },
+        [&](int l, void** o, int64_t* ld) { *o = ws + p.off_P[l]; *ld = p.ldp[l]; },
+        grad_id, layers, r, seed, static_cast<uint32_t>(proj_step), bf16, false, s);
+    if (st) return st;
+    // 2. Xt_l = P_l A_l^T, per sample [r][T]
+    ProjArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.B = static_cast<int32_t>(B);
+    a.T = static_cast<int32_t>(T);
+    a.r = r;
+    a.ldt = static_cast<int32_t>(p.ldt);
+    int blocks = 0;
+    bool vec = true;
+    for (int l = l0; l < l1; ++l) {
+      ProjLayer& L = a.L[l - l0];
+      L.A = layers[l].A;
+      L.P = ws + p.off_P[l];
+      L.Xt = ws + p.off_Xt[l];
+      L.d_in = static_cast<int32_t>(layers[l].d_in);
+      L.ldp = static_cast<int32_t>(p.ldp[l]);
+      L.m_tiles = p.m_tiles_proj[l];
+      L.n_tiles = p.n_tiles_proj[l];
+      L.block0 = blocks;
+      blocks += L.m_tiles * L.n_tiles;
+      vec = vec && layers[l].d_in % vec_elems == 0 && aligned(layers[l].A, 16);
+    }
+    a.n_layers = l1 - l0;
+    a.n_blocks = blocks;
+    if ((st = timed(K_PROJ, s, [&] { return launch_proj(a, bf16, vec, s); }))) return st;
+  }
+
+  // 3. squared-norm partials of every (sample, layer, tile)
+  auto fill_samp = [&](SampArgs& a, int l0, int l1, bool sum, bool* pair) {
+    std::memset(&a, 0, sizeof(a));
+    a.B = static_cast<int32_t>(B);
+    a.T = static_cast<int32_t>(T);
+    a.r = r;
+    a.ldt = static_cast<int32_t>(p.ldt);
+    a.groups = p.groups;
+    a.per_group = p.per_group;
+    a.n_slots = p.n_slots;
+    a.norm_part = norm_part;
+    a.scales = scales;
+    int blocks = 0;
+    *pair = true;
+    for (int l = l0; l < l1; ++l) {
+      SampLayer& L = a.L[l - l0];
+      L.dY = layers[l].dY;
+      L.Xt = ws + p.off_Xt[l];
+      L.part = reinterpret_cast<float*>(ws + p.off_part[l]);
+      L.d_out = static_cast<int32_t>(layers[l].d_out);
+      L.m_tiles = p.m_tiles_s[l];
+      L.n_tiles = p.n_tiles_s[l];
+      L.slot0 = p.slot0[l];
+      L.block0 = blocks;
+      blocks += L.m_tiles * L.n_tiles * (sum ? p.groups : static_cast<int32_t>(B));
+      *pair = *pair && layers[l].d_out % 2 == 0 && aligned(layers[l].dY, 4);
+    }
+    a.n_layers = l1 - l0;
+    a.n_blocks = blocks;
+  };
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int l1 = std::min(n_layers, l0 + kMaxLayers);
+    SampArgs a;
+    bool pair;
+    fill_samp(a, l0, l1, false, &pair);
+    if ((st = timed(K_NORM, s, [&] { return launch_samp_norm(a, bf16, pair, s); })))
+      return st;
+  }
+  // 4. per-sample norm and clip factor (needs every layer's partials)
+  {
+    ScaleArgs a;
+    a.norm_part = norm_part;
+    a.n_slots = p.n_slots;
+    a.clip_C = clip_C;
+    a.scales = scales;
+    a.norms_out = sample_norms;
+    if ((st = timed(K_SCALE, s, [&] { return launch_scale(a, static_cast<int>(B), s); })))
+      return st;
+  }
+  // 5-6. clipped sum over samples, then noise and 1/B
+  const double noise = sigma == 0.0f ? 0.0 : static_cast<double>(sigma) * clip_C;
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int l1 = std::min(n_layers, l0 + kMaxLayers);
+    SampArgs a;
+    bool pair;
+    fill_samp(a, l0, l1, true, &pair);
+    if ((st = timed(K_SUM, s, [&] { return launch_samp_sum(a, bf16, pair, s); })))
+      return st;
+    FinArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.groups = p.groups;
+    f.noise_scale = static_cast<float>(noise);
+    f.inv_B = static_cast<float>(1.0 / static_cast<double>(B));
+    f.k0 = static_cast<uint32_t>(seed);
+    f.k1 = static_cast<uint32_t>(seed >> 32);
+    f.step_word = static_cast<uint32_t>(step);
+    int blocks = 0;
+    for (int l = l0; l < l1; ++l) {
+      FinLayer& L = f.L[l - l0];
+      L.part = reinterpret_cast<const float*>(ws + p.off_part[l]);
+      L.out = layers[l].G_priv;
+      L.n_elem = static_cast<int32_t>(static_cast<int64_t>(r) * layers[l].d_out);
+      L.layer_id = layers[l].layer_id;
+      L.block0 = blocks;
+      blocks += static_cast<int>(ceil_div(ceil_div(L.n_elem, 4), kThreads));
+    }
+    f.n_layers = l1 - l0;
+    if ((st = timed(K_FIN, s, [&] { return launch_fin(f, blocks, s); }))) return st;
+  }
+  return DPG_OK;
+}
+
+int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
+                         int32_t r, int32_t dtype, float lr, float beta1,
+                         float beta2, float eps, uint64_t seed, uint64_t step,
+                         uint64_t proj_step, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = validate_adam_shapes(params, n_layers, r, dtype);
+  if (st) return st;
+  for (int i = 0; i < n_layers; ++i)
+    if (!params[i].G_priv || !params[i].W || !params[i].m || !params[i].v)
+      return fail(DPG_ERR_INVALID_ARG,
+                  "NULL data pointer in layer index " + std::to_string(i));
+  if (!(lr > 0.0f) || std::isinf(lr))
+    return fail(DPG_ERR_INVALID_ARG, "lr must be finite and > 0");
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(DPG_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
+  if (!(eps > 0.0f) || std::isinf(eps))
+    return fail(DPG_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if ((st = check_seed_steps(step, proj_step))) return st;
+  const AdamPlan p = plan_adam(params, n_layers, r, dtype);
+  if ((st = check_workspace(workspace, workspace_bytes, p.total))) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const bool bf16 = dtype == DPG_BF16;
+  const double t = static_cast<double>(step);
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int l1 = std::min(n_layers, l0 + kMaxLayers);
+    // 5. Adam on [r][d_out]; U written transposed for the back-projection
+    AdamArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.r = r;
+    a.ldr = static_cast<int32_t>(p.ldr);
+    a.beta1 = beta1;
+    a.beta2 = beta2;
+    a.one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(beta1));
+    a.one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(beta2));
+    a.bc1 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta1), t));
+    a.bc2 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta2), t));
+    a.eps = eps;
+    int blocks = 0;
+    for (int l = l0; l < l1; ++l) {
+      AdamLayer& L = a.L[l - l0];
+      L.g = params[l].G_priv;
+      L.m = params[l].m;
+      L.v = params[l].v;
+      L.Ut = ws + p.off_Ut[l];
+      L.d_out = static_cast<int32_t>(params[l].d_out);
+      L.n_elem = static_cast<int32_t>(static_cast<int64_t>(r) * params[l].d_out);
+      L.block0 = blocks;
+      blocks += static_cast<int>(ceil_div(ceil_div(L.n_elem, 4), kThreads));
+    }
+    a.n_layers = l1 - l0;
+    if ((st = timed(K_ADAM, s, [&] { return launch_adam(a, blocks, bf16, s); }))) return st;
+    // P_l regenerated, transposed [d_in][ldr]
+    st = enqueue_gen_p(
+        l0, l1, [&](int l) { return params[l].d_in; },
+        [&](int l, void** o, int64_t* ld) { *o = ws + p.off_Pt[l]; *ld = p.ldr; },
+        param_id, params, r, seed, static_cast<uint32_t>(proj_step), bf16, true, s);
+    if (st) return st;
+    // 6. W -= lr P^T U
+    BackArgs b;
+    std::memset(&b, 0, sizeof(b));
+    b.r = r;
+    b.ldr = static_cast<int32_t>(p.ldr);
+    b.lr = lr;
+    blocks = 0;
+    for (int l = l0; l < l1; ++l) {
+      BackLayer& L = b.L[l - l0];
+      L.Pt = ws + p.off_Pt[l];
+      L.Ut = ws + p.off_Ut[l];
+      L.W = params[l].W;
+      L.d_in = static_cast<int32_t>(params[l].d_in);
+      L.d_out = static_cast<int32_t>(params[l].d_out);
+      L.m_tiles = static_cast<int32_t>(ceil_div(params[l].d_in, kBackBM));
+      L.n_tiles = static_cast<int32_t>(ceil_div(params[l].d_out, kBackBN));
+      L.block0 = blocks;
+      blocks += L.m_tiles * L.n_tiles;
+    }
+    b.n_layers = l1 - l0;
+    b.n_blocks = blocks;
+    if ((st = timed(K_BACK, s, [&] { return launch_back(b, bf16, s); }))) return st;
+  }
+  return DPG_OK;
+}
+
+int dpg_timing_enable(int on) {
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  g_timing_on = on != 0;
+  return DPG_OK;
+}
+
+int dpg_timing_read(double* total_ms, int64_t* launches, int32_t n_kinds,
+                    int reset) {
+  g_last_error.clear();
+  std::vector<TimedLaunch> pend;
+  {
+    std::lock_guard<std::mutex> g(g_timing_mu);
+    pend.swap(g_pending);
+  }
+  hipError_t err = hipSuccess;
+  double add[K_COUNT] = {};
+  int64_t cnt[K_COUNT] = {};
+  for (const TimedLaunch& t : pend) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    if (e == hipSuccess) {
+      add[t.kind] += ms;
+      cnt[t.kind] += 1;
+    }
+    hipEventDestroy(t.start);
+    hipEventDestroy(t.stop);
+  }
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  for (int k = 0; k < K_COUNT; ++k) {
+    g_total_ms[k] += add[k];
+    g_launches[k] += cnt[k];
+  }
+  for (int k = 0; k < K_COUNT && k < n_kinds; ++k) {
+    if (total_ms) total_ms[k] = g_total_ms[k];
+    if (launches) launches[k] = g_launches[k];
+  }
+  if (reset)
+    for (int k = 0; k < K_COUNT; ++k) {
+      g_total_ms[k] = 0.0;
+      g_launches[k] = 0;
+    }
+  if (err != hipSuccess)
+    return fail(DPG_ERR_HIP, std::string("timing events: ") + hipGetErrorString(err));
+  return DPG_OK;
+}
+
+const char* dpg_kernel_name(int kind) {
+  return (kind >= 0 && kind < K_COUNT) ? kKindName[kind] : "";
+}
+
+int dpg_philox_normals(uint64_t seed, uint32_t layer_id, uint32_t step_word,
+                       uint32_t tag, uint64_t start, uint64_t n, float* z_out,
+                       uint32_t* words_out, void* stream) {
+  g_last_error.clear();
+  if (n == 0) return DPG_OK;
+  if (!z_out) return fail(DPG_ERR_INVALID_ARG, "z_out is NULL");
+  if (start + n > kMaxU32 || start + n < start)
+    return fail(DPG_ERR_INVALID_ARG, "start + n must be < 2^32");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return check(launch_philox_normals(static_cast<uint32_t>(seed),
+                                     static_cast<uint32_t>(seed >> 32), layer_id,
+                                     step_word, tag, static_cast<uint32_t>(start),
+                                     static_cast<uint32_t>(n), z_out, words_out, s),
+               "philox_normals", s);
+}
+
+}  // extern "C"

@@ -1,0 +1,454 @@
+// Device building blocks for the DP-GRAPE kernels on gfx950 (CDNA4).
+//
+//  * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+//    Easy as 1, 2, 3", SC'11) and Box-Muller normals: the generator that
+//    regenerates the projection P and draws the noise Z from a seed, as the
+//    method requires of P ("Memory-Efficient Differentially Private Training
+//    with Gradient Random Projection", technical summary, Methodology, design
+//    choice 1). Stream layout: key = seed, counter = (e >> 2, layer_id,
+//    step word, tag); u(x) = (2 (x >> 9) + 1) 2^-24; element e takes entry
+//    e & 3 of (R0 cos t0, R0 sin t0, R1 cos t1, R1 sin t1).
+//  * A 256-thread (4 x wave64) LDS-staged tile engine around the
+//    v_mfma_f32_32x32x16_bf16 (bf16 operands) and v_mfma_f32_32x32x2_f32
+//    (fp32 operands) matrix-core instructions, fp32 accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dpg_internal.hpp"
+
+namespace dpg {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// ---------------------------------------------------------------- random --
+
+// Ten Philox rounds: each round multiplies c0 and c2 by the two round
+// constants (32x32 -> 64 bit), and the key is bumped by the Weyl constants
+// between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1,
+                                              uint32_t c2, uint32_t c3,
+                                              uint32_t k0, uint32_t k1,
+                                              uint32_t out[4]) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo0 = c0 * 0xD2511F53u;
+    const uint32_t hi0 = __umulhi(c0, 0xD2511F53u);
+    const uint32_t lo1 = c2 * 0xCD9E8D57u;
+    const uint32_t hi1 = __umulhi(c2, 0xCD9E8D57u);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// Uniform in (0, 1): (2 (x >> 9) + 1) * 2^-24. The odd integer is < 2^24, so
+// the conversion and the scaling are exact in fp32.
+__device__ __forceinline__ float uniform_open01(uint32_t x) {
+  return static_cast<float>(((x >> 9) << 1) | 1u) * 5.9604644775390625e-08f;
+}
+
+// Box-Muller on the pairs (w0, w1) and (w2, w3). sincospif takes the angle
+// in half-turns, so 2u is passed exactly (no rounding of 2 pi u).
+__device__ __forceinline__ void box_muller4(const uint32_t w[4], float z[4]) {
+  const float r0 = sqrtf(-2.0f * logf(uniform_open01(w[0])));
+  const float r1 = sqrtf(-2.0f * logf(uniform_open01(w[2])));
+  float s0, c0, s1, c1;
+  sincospif(2.0f * uniform_open01(w[1]), &s0, &c0);
+  sincospif(2.0f * uniform_open01(w[3]), &s1, &c1);
+  z[0] = r0 * c0;
+  z[1] = r0 * s0;
+  z[2] = r1 * c1;
+  z[3] = r1 * s1;
+}
+
+struct StreamKey {
+  uint32_t k0, k1;       // seed low / high word
+  uint32_t step_word;    // proj_step (tag 0) or step (tag 1)
+  uint32_t tag;          // 0 = projection P, 1 = noise Z
+};
+
+// The four normals of counter c of one layer's stream.
+__device__ __forceinline__ void normals_at(const StreamKey& key,
+                                           uint32_t layer_id, uint32_t c,
+                                           float z[4]) {
+  uint32_t w[4];
+  philox4x32_10(c, layer_id, key.step_word, key.tag, key.k0, key.k1, w);
+  box_muller4(w, z);
+}
+
+// ------------------------------------------------------------ data types --
+
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
+
+__device__ __forceinline__ float to_float(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_float(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_float(float x);
+template <> __device__ __forceinline__ bf16 from_float<bf16>(float x) {
+  return static_cast<bf16>(x);  // round to nearest even
+}
+template <> __device__ __forceinline__ float from_float<float>(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ T zero_val() { return from_float<T>(0.0f); }
+
+// ----------------------------------------------------------- tile engine --
+//
+// A block computes C[BM x BN] = sum_k Aop[m][k] * Bop[n][k] with both operands
+// staged in LDS as K-contiguous rows (sA[m][k], sB[n][k]). The four waves
+// split the tile 2 x 2; wave w owns rows [(w & 1) * BM/2, +BM/2) and columns
+// [(w >> 1) * BN/2, +BN/2) as MB x NB blocks of 32 x 32.
+//
+// Accumulator layout of a 32x32 block (v_mfma_f32_32x32x*): lane l holds
+// column (l & 31) and, in register i = 0..15, row 8*(i/4) + 4*(l >> 5) + (i & 3).
+
+template <typename T, int BK>
+struct LdsRow {
+  static constexpr int kPad = 16 / sizeof(T);  // 16-byte pad per row
+  static constexpr int kStride = BK + kPad;    // elements per LDS row
+};
+
+template <typename T, int BM, int BN, int BK>
+struct TileShape {
+  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
+  static constexpr int MB = WTM / 32, NB = WTN / 32;
+  static constexpr int S = LdsRow<T, BK>::kStride;
+  static_assert(MB >= 1 && NB >= 1, "tile too small");
+  static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+};
+
+template <int MB, int NB>
+struct Acc {
+  f32x16 v[MB][NB];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[a][b][i] = 0.0f;
+  }
+};
+
+// One BK-deep step of matrix-core work from LDS.
+template <typename T, int BM, int BN, int BK> struct Mma;
+
+template <int BM, int BN, int BK>
+struct Mma<bf16, BM, BN, BK> {
+  typedef TileShape<bf16, BM, BN, BK> Sh;
+  __device__ __forceinline__ static void run(const bf16* sA, const bf16* sB,
+                                             Acc<Sh::MB, Sh::NB>& acc, int wm,
+                                             int wn, int lane) {
+    const int r = lane & 31, kq = (lane >> 5) * 8;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 a[Sh::MB], b[Sh::NB];
+#pragma unroll
+      for (int mb = 0; mb < Sh::MB; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(
+            sA + (wm * Sh::WTM + mb * 32 + r) * Sh::S + kk + kq);
+#pragma unroll
+      for (int nb = 0; nb < Sh::NB; ++nb)
+        b[nb] = *reinterpret_cast<const bf16x8*>(
+            sB + (wn * Sh::WTN + nb * 32 + r) * Sh::S + kk + kq);
+#pragma unroll
+      for (int mb = 0; mb < Sh::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < Sh::NB; ++nb)
+          acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a[mb], b[nb], acc.v[mb][nb], 0, 0, 0);
+    }
+  }
+};
+
+template <int BM, int BN, int BK>
+struct Mma<float, BM, BN, BK> {
+  typedef TileShape<float, BM, BN, BK> Sh;
+  __device__ __forceinline__ static void run(const float* sA, const float* sB,
+                                             Acc<Sh::MB, Sh::NB>& acc, int wm,
+                                             int wn, int lane) {
+    const int r = lane & 31, kq = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      float a[Sh::MB], b[Sh::NB];
+#pragma unroll
+      for (int mb = 0; mb < Sh::MB; ++mb)
+        a[mb] = sA[(wm * Sh::WTM + mb * 32 + r) * Sh::S + kk + kq];
+#pragma unroll
+      for (int nb = 0; nb < Sh::NB; ++nb)
+        b[nb] = sB[(wn * Sh::WTN + nb * 32 + r) * Sh::S + kk + kq];
+#pragma unroll
+      for (int mb = 0; mb < Sh::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < Sh::NB; ++nb)
+          acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              a[mb], b[nb], acc.v[mb][nb], 0, 0, 0);
+    }
+  }
+};
+
+// Loads ROWS x BK of a K-contiguous source (row stride ld elements; rows
+// >= nrows and columns >= K read as zero) into registers, then into LDS
+// sX[row][k]. VEC: 16-byte loads (needs ld % (16/sizeof(T)) == 0 and a
+// 16-byte aligned base); otherwise element loads.
+template <typename T, int ROWS, int BK, bool VEC>
+struct RowsLoader {
+  typedef typename Vec16<T>::type V;
+  static constexpr int VN = Vec16<T>::N;
+  static constexpr int CPR = BK / VN;               // chunks per row
+  static constexpr int PER = ROWS * CPR / kThreads; // chunks per thread
+  static_assert(PER >= 1 && (ROWS * CPR) % kThreads == 0, "bad tiling");
+  static constexpr int S = LdsRow<T, BK>::kStride;
+
+  const T* base;
+  int64_t ld;
+  int nrows;
+  int K;
+  V reg[PER];
+
+  __device__ __forceinline__ void load(int k0, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int ci = tid + p * kThreads;
+      const int row = ci / CPR;
+      const int k = k0 + (ci % CPR) * VN;
+      V v;
+#pragma unroll
+      for (int q = 0; q < VN; ++q) v[q] = zero_val<T>();
+      if (row < nrows && k < K) {
+        const T* src = base + static_cast<int64_t>(row) * ld + k;
+        if constexpr (VEC) {
+          v = *reinterpret_cast<const V*>(src);
+          if (k + VN > K) {
+#pragma unroll
+            for (int q = 0; q < VN; ++q)
+              if (k + q >= K) v[q] = zero_val<T>();
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < VN; ++q)
+            if (k + q < K) v[q] = src[q];
+        }
+      }
+      reg[p] = v;
+    }
+  }
+
+  __device__ __forceinline__ void store(T* sX, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int ci = tid + p * kThreads;
+      const int row = ci / CPR;
+      const int kc = (ci % CPR) * VN;
+      *reinterpret_cast<V*>(sX + row * S + kc) = reg[p];
+    }
+  }
+};
+
+// Loads BK x COLS of an N-contiguous source X[k][n] (row stride ld) and
+// stores it transposed into LDS sX[n][k], so that the contraction index k
+// ends up contiguous for the matrix cores. Rows >= K and columns >= ncols
+// read as zero. Each thread gathers 8 consecutive k of one or two columns.
+template <typename T, int COLS, int BK, bool PAIR>
+struct ColsLoader;
+
+// bf16, PAIR: a thread loads 32-bit words (2 columns) from 8 consecutive
+// rows and splits them into two 8-element k-vectors (needs an even ld, an
+// even column offset and a 4-byte aligned base).
+template <int COLS, int BK>
+struct ColsLoader<bf16, COLS, BK, true> {
+  static constexpr int S = LdsRow<bf16, BK>::kStride;
+  static constexpr int ITEMS = (COLS / 2) * (BK / 8);
+  static constexpr int PER = ITEMS / kThreads;
+  static_assert(PER >= 1 && ITEMS % kThreads == 0, "bad tiling");
+  const bf16* base;
+  int64_t ld;
+  int ncols;
+  int K;
+  uint32_t w[PER][8];
+
+  __device__ __forceinline__ void load(int k0, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int it = tid + p * kThreads;
+      const int c = (it % (COLS / 2)) * 2;
+      const int k = k0 + (it / (COLS / 2)) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t x = 0;
+        if (k + j < K) {
+          const bf16* src = base + static_cast<int64_t>(k + j) * ld + c;
+          if (c + 1 < ncols) {
+            x = *reinterpret_cast<const uint32_t*>(src);
+          } else if (c < ncols) {
+            x = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(src));
+          }
+        }
+        w[p][j] = x;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16* sX, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int it = tid + p * kThreads;
+      const int c = (it % (COLS / 2)) * 2;
+      const int kc = (it / (COLS / 2)) * 8;
+      u32x4 lo, hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = w[p][2 * j], b = w[p][2 * j + 1];
+        lo[j] = (a & 0xFFFFu) | (b << 16);
+        hi[j] = (a >> 16) | (b & 0xFFFF0000u);
+      }
+      *reinterpret_cast<u32x4*>(sX + c * S + kc) = lo;
+      *reinterpret_cast<u32x4*>(sX + (c + 1) * S + kc) = hi;
+    }
+  }
+};
+
+// bf16, element loads (odd row stride or unaligned base).
+template <int COLS, int BK>
+struct ColsLoader<bf16, COLS, BK, false> {
+  static constexpr int S = LdsRow<bf16, BK>::kStride;
+  static constexpr int ITEMS = COLS * (BK / 8);
+  static constexpr int PER = ITEMS / kThreads;
+  static_assert(PER >= 1 && ITEMS % kThreads == 0, "bad tiling");
+  const bf16* base;
+  int64_t ld;
+  int ncols;
+  int K;
+  uint16_t h[PER][8];
+
+  __device__ __forceinline__ void load(int k0, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int it = tid + p * kThreads;
+      const int c = it % COLS;
+      const int k = k0 + (it / COLS) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint16_t x = 0;
+        if (k + j < K && c < ncols)
+          x = *reinterpret_cast<const uint16_t*>(
+              base + static_cast<int64_t>(k + j) * ld + c);
+        h[p][j] = x;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16* sX, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int it = tid + p * kThreads;
+      const int c = it % COLS;
+      const int kc = (it / COLS) * 8;
+      u32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = static_cast<uint32_t>(h[p][2 * j]) |
+               (static_cast<uint32_t>(h[p][2 * j + 1]) << 16);
+      *reinterpret_cast<u32x4*>(sX + c * S + kc) = v;
+    }
+  }
+};
+
+// fp32: a thread loads one column from 4 consecutive rows (4-byte loads,
+// consecutive lanes on consecutive columns) and stores one 16-byte k-vector.
+template <int COLS, int BK, bool PAIR>
+struct ColsLoader<float, COLS, BK, PAIR> {
+  static constexpr int S = LdsRow<float, BK>::kStride;
+  static constexpr int ITEMS = COLS * (BK / 4);
+  static constexpr int PER = ITEMS / kThreads;
+  static_assert(PER >= 1 && ITEMS % kThreads == 0, "bad tiling");
+  const float* base;
+  int64_t ld;
+  int ncols;
+  int K;
+  f32x4 reg[PER];
+
+  __device__ __forceinline__ void load(int k0, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int it = tid + p * kThreads;
+      const int c = it % COLS;
+      const int k = k0 + (it / COLS) * 4;
+      f32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = (k + j < K && c < ncols)
+                   ? base[static_cast<int64_t>(k + j) * ld + c]
+                   : 0.0f;
+      reg[p] = v;
+    }
+  }
+
+  __device__ __forceinline__ void store(float* sX, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int it = tid + p * kThreads;
+      const int c = it % COLS;
+      const int kc = (it / COLS) * 4;
+      *reinterpret_cast<f32x4*>(sX + c * S + kc) = reg[p];
+    }
+  }
+};
+
+// Runs the K loop [k_begin, k_end) in BK steps: the next step's global loads
+// are issued before the current step's matrix-core work.
+template <typename T, int BM, int BN, int BK, class LA, class LB>
+__device__ __forceinline__ void k_loop(LA& la, LB& lb, T* sA, T* sB,
+                                       Acc<TileShape<T, BM, BN, BK>::MB,
+                                           TileShape<T, BM, BN, BK>::NB>& acc,
+                                       int k_begin, int k_end, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  if (k_begin >= k_end) return;
+  la.load(k_begin, tid);
+  lb.load(k_begin, tid);
+  for (int k0 = k_begin; k0 < k_end; k0 += BK) {
+    __syncthreads();  // previous step finished reading LDS
+    la.store(sA, tid);
+    lb.store(sB, tid);
+    __syncthreads();
+    if (k0 + BK < k_end) {
+      la.load(k0 + BK, tid);
+      lb.load(k0 + BK, tid);
+    }
+    Mma<T, BM, BN, BK>::run(sA, sB, acc, wm, wn, lane);
+  }
+}
+
+// Row (within the block tile) of accumulator register i of block (mb, .).
+template <int WTM>
+__device__ __forceinline__ int acc_row(int wm, int mb, int i, int lane) {
+  return wm * WTM + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+template <int WTN>
+__device__ __forceinline__ int acc_col(int wn, int nb, int lane) {
+  return wn * WTN + nb * 32 + (lane & 31);
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).
+// This maps the hardware block id to a logical id so that consecutive
+// logical blocks run on the same XCD; gridDim.x must be a multiple of 8.
+__device__ __forceinline__ int xcd_logical_block() {
+  const int per = gridDim.x >> 3;
+  return (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+}
+
+}  // namespace dpg

@@ -1,0 +1,203 @@
+/*
+ * dpg.h - C ABI of the DP-GRAPE private update step on one AMD MI355X (gfx950).
+ *
+ * The method ("Memory-Efficient Differentially Private Training with Gradient
+ * Random Projection", gist.science technical summary, Methodology): during the
+ * backward pass every sample's linear-layer gradient G_i = A_i^T dY_i is
+ * projected onto a random Gaussian subspace P that is regenerated from a seed
+ * (design choice 1) before any privatisation (design choice 2); the projected
+ * per-sample gradients are clipped by their global norm, summed over the
+ * batch and noised; Adam runs on the projected gradient with its moments in
+ * the projected space (design choice 3); and the update is back-projected
+ * into the weights (closing paragraph of Methodology).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - A layer is y = x W with W of shape [d_in][d_out] (row-major). Its
+ *   per-sample gradient is A_i^T dY_i, so P has shape [r][d_in] and acts on
+ *   the d_in side.
+ * - P[j][k] = z(seed, layer_id, proj_step, tag 0, e = j*d_in + k) / sqrt(r) and
+ *   the noise Z[j][n] = z(seed, layer_id, step, tag 1, e = j*d_out + n), where
+ *   z(...) is a standard normal from Philox4x32-10 (Salmon et al., SC'11;
+ *   key = seed, counter = (e >> 2, layer_id, step word, tag)) followed by
+ *   Box-Muller on the uniforms u(x) = (2*(x >> 9) + 1) * 2^-24; element e
+ *   takes entry e & 3 of (R0 cos t0, R0 sin t0, R1 cos t1, R1 sin t1).
+ *   P is never stored between calls: each call regenerates it.
+ * - All pointers inside the structs and all data pointers are DEVICE pointers
+ *   on the current HIP device, except the struct arrays themselves, which are
+ *   host memory read only during the call. The caller owns every buffer; the
+ *   library allocates no device memory, keeps no pointer after the call
+ *   returns, and keeps no state apart from the optional kernel-timing
+ *   diagnostics below.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   the call returns before it completes. Buffers, including the workspace,
+ *   must stay alive until the stream reaches that point; one workspace must
+ *   not serve two calls in flight at once.
+ * - Errors: invalid arguments return DPG_ERR_INVALID_ARG, a missing or small
+ *   workspace DPG_ERR_WORKSPACE; both are detected before anything is
+ *   enqueued. A failed launch returns DPG_ERR_HIP (earlier kernels of the
+ *   same call may already be enqueued). dpg_last_error() then describes the
+ *   failure. No C++ exception crosses this interface.
+ * - Inputs must not alias outputs. NaN and Inf in the data are not checked
+ *   and propagate.
+ */
+#ifndef DPG_H_
+#define DPG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DPG_OK = 0,
+  DPG_ERR_INVALID_ARG = 1,
+  DPG_ERR_WORKSPACE = 2,
+  DPG_ERR_UNSUPPORTED = 3,
+  DPG_ERR_HIP = 4
+} dpg_status;
+
+/* Element type of the activations A and output gradients dY. Everything
+ * else (G_priv, W, m, v, sample norms) is fp32. */
+typedef enum { DPG_FP32 = 0, DPG_BF16 = 1 } dpg_dtype;
+
+/* One linear layer's inputs to dpg_project_clip_noise. */
+typedef struct {
+  int64_t d_in;        /* > 0 */
+  int64_t d_out;       /* > 0 */
+  uint32_t layer_id;   /* unique within the call; keys P and Z */
+  uint32_t reserved;   /* set to 0 */
+  const void* A;       /* device, [B][T][d_in] row-major, dtype */
+  const void* dY;      /* device, [B][T][d_out] row-major, dtype */
+  float* G_priv;       /* device out, [r][d_out] fp32 */
+} dpg_layer_grad;
+
+/* One linear layer's state for dpg_adam_backproject. */
+typedef struct {
+  int64_t d_in;        /* > 0 */
+  int64_t d_out;       /* > 0 */
+  uint32_t layer_id;   /* the same id that was used to project this layer */
+  uint32_t reserved;   /* set to 0 */
+  const float* G_priv; /* device, [r][d_out] fp32 privatised projected grad */
+  float* W;            /* device, [d_in][d_out] fp32, updated in place */
+  float* m;            /* device, [r][d_out] fp32 Adam first moment, in place */
+  float* v;            /* device, [r][d_out] fp32 Adam second moment, in place */
+} dpg_layer_param;
+
+/*
+ * dpg_project_workspace_size: bytes of device workspace that
+ * dpg_project_clip_noise needs for these arguments (written to *bytes).
+ * Validates the same shape arguments; pointers inside `layers` are not read.
+ */
+int dpg_project_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
+                               int64_t B, int64_t T, int32_t r, int32_t dtype,
+                               size_t* bytes);
+
+/*
+ * dpg_project_clip_noise: steps 1-4 of the private update for a batch.
+ *   (Methodology design choices 1 and 2; closing paragraph of Methodology:
+ *    the projected gradients are aggregated, clipped and noised.)
+ * For every layer l and sample i:
+ *     Ghat_il = P_l (A_il^T dY_il)                         [r][d_out]
+ *   computed as (A_il P_l^T)^T dY_il;
+ *     n_i = sqrt(sum_l ||Ghat_il||_F^2)   (one norm across all layers)
+ *     s_i = min(1, C / n_i)   (s_i = 1 when n_i = 0 or C = +inf)
+ *     G_priv_l = (sum_i s_i Ghat_il + sigma * C * Z_l) / B
+ *   (the noise term is absent when sigma = 0).
+ * Arguments:
+ *   layers, n_layers  host array of n_layers >= 1 layer descriptors
+ *   B, T              batch size and tokens per sample (>= 1)
+ *   r                 projection rank (>= 1); r*d_in and r*d_out < 2^32
+ *   dtype             DPG_FP32 or DPG_BF16 (element type of A and dY)
+ *   clip_C            clip threshold C > 0, or +INFINITY for no clipping
+ *   sigma             noise multiplier >= 0 and finite; must be 0 if C is inf
+ *   seed              64-bit key of both random streams
+ *   step              optimiser step t (1 <= step < 2^32); keys the noise
+ *   proj_step         keys P (< 2^32); pass the same value to
+ *                     dpg_adam_backproject. proj_step = step draws a new P
+ *                     every step.
+ *   sample_norms      device out [B] fp32 of the pre-clip norms n_i, or NULL
+ *   workspace         device scratch of at least
+ *                     dpg_project_workspace_size(...) bytes, 256-byte aligned
+ *   stream            hipStream_t to enqueue on
+ */
+int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
+                           int64_t B, int64_t T, int32_t r, int32_t dtype,
+                           float clip_C, float sigma, uint64_t seed,
+                           uint64_t step, uint64_t proj_step,
+                           float* sample_norms, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * dpg_adam_workspace_size: bytes of device workspace dpg_adam_backproject
+ * needs (written to *bytes). Element type of the internal bf16/fp32 operands
+ * follows `dtype` (DPG_BF16 rounds P and the Adam direction to bf16 for the
+ * matrix cores; DPG_FP32 keeps them fp32).
+ */
+int dpg_adam_workspace_size(const dpg_layer_param* params, int32_t n_layers,
+                            int32_t r, int32_t dtype, size_t* bytes);
+
+/*
+ * dpg_adam_backproject: steps 5-6 (Methodology design choice 3; closing
+ * paragraph of Methodology: a projected Adam rule updates the parameters).
+ * For every layer, with t = step and g = G_priv:
+ *     m <- beta1 m + (1 - beta1) g
+ *     v <- beta2 v + (1 - beta2) g^2
+ *     U  = (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ *     W <- W - lr P^T U          (P regenerated from seed, layer_id, proj_step)
+ * Arguments: lr > 0 finite, 0 <= beta1, beta2 < 1, eps > 0, step >= 1
+ * (< 2^32), proj_step as passed to dpg_project_clip_noise. m and v must be
+ * zero before step 1. dtype selects the operand precision of P^T U.
+ */
+int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
+                         int32_t r, int32_t dtype, float lr, float beta1,
+                         float beta2, float eps, uint64_t seed, uint64_t step,
+                         uint64_t proj_step, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * dpg_philox_normals: the random stream both calls draw from, exposed so it
+ * can be checked on its own. For e in [start, start + n):
+ *     z_out[e - start] = z(seed, layer_id, step_word, tag, e)
+ * and, when words_out is not NULL, words_out[4*(c - (start >> 2)) + q] is
+ * output word q of Philox4x32-10 at counter c = (e >> 2, layer_id,
+ * step_word, tag) for every counter c touched. z_out: device [n] fp32;
+ * words_out: device [4 * (((start + n - 1) >> 2) - (start >> 2) + 1)] u32.
+ * start + n must be < 2^32; n = 0 is a no-op.
+ */
+int dpg_philox_normals(uint64_t seed, uint32_t layer_id, uint32_t step_word,
+                       uint32_t tag, uint64_t start, uint64_t n, float* z_out,
+                       uint32_t* words_out, void* stream);
+
+/*
+ * Kernel-timing diagnostics. While enabled (process-wide), every kernel that
+ * dpg_project_clip_noise / dpg_adam_backproject enqueue is bracketed by a
+ * pair of HIP events recorded on the call's own stream. dpg_timing_read waits
+ * for those events, adds each launch's elapsed time to the total of its
+ * kernel kind and returns, for kinds 0 .. n_kinds-1, the total milliseconds
+ * and the number of launches since the last reset (then clears them when
+ * reset != 0). Kinds: see dpg_kernel_name; DPG_N_KERNEL_KINDS of them.
+ * Enabling adds host work per launch; leave it off when timing whole steps.
+ */
+#define DPG_N_KERNEL_KINDS 9
+int dpg_timing_enable(int on);
+int dpg_timing_read(double* total_ms, int64_t* launches, int32_t n_kinds,
+                    int reset);
+const char* dpg_kernel_name(int kind);
+
+/* Static text for a status code. */
+const char* dpg_status_string(int status);
+
+/* Description of the most recent failure in the calling thread ("" if none). */
+const char* dpg_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int dpg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPG_H_ */

@@ -1,0 +1,173 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol that
+include/dpg.h declares, and rejects invalid arguments before touching HIP."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import dp_grape_projection_amd as dpg
+from dp_grape_projection_amd.binding import LayerGrad, LayerParam
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dpg.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dpg.library_path()):
+        pytest.skip("libdpg.so not built")
+    return dpg.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dpg_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dpg_project_clip_noise", "dpg_adam_backproject",
+              "dpg_project_workspace_size", "dpg_adam_workspace_size",
+              "dpg_philox_normals", "dpg_status_string", "dpg_last_error",
+              "dpg_version"):
+        assert n in names
+    assert sorted(dpg.EXPORTED) == names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.dpg_version() == 10000
+
+
+def test_struct_layout_matches_header():
+    # int64 d_in, d_out; u32 layer_id, reserved; three / four pointers
+    assert ctypes.sizeof(LayerGrad) == 8 + 8 + 4 + 4 + 3 * 8
+    assert ctypes.sizeof(LayerParam) == 8 + 8 + 4 + 4 + 4 * 8
+    assert LayerGrad.A.offset == 24 and LayerParam.G_priv.offset == 24
+
+
+def _grads(shapes, ids=None, ptr=0x1000):
+    arr = (LayerGrad * len(shapes))()
+    for i, (a, b) in enumerate(shapes):
+        arr[i].d_in, arr[i].d_out = a, b
+        arr[i].layer_id = i if ids is None else ids[i]
+        arr[i].A = arr[i].dY = arr[i].G_priv = ptr
+    return arr
+
+
+def _params(shapes, ids=None, ptr=0x1000):
+    arr = (LayerParam * len(shapes))()
+    for i, (a, b) in enumerate(shapes):
+        arr[i].d_in, arr[i].d_out = a, b
+        arr[i].layer_id = i if ids is None else ids[i]
+        arr[i].G_priv = arr[i].W = arr[i].m = arr[i].v = ptr
+    return arr
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.dpg_status_string(code).startswith(b"DPG_")
+    assert b"unknown" in lib.dpg_status_string(99)
+
+
+def test_workspace_size_queries(lib):
+    out = ctypes.c_size_t(0)
+    st = lib.dpg_project_workspace_size(_grads([(768, 3072), (3072, 768)]), 2,
+                                        32, 128, 128, 1, ctypes.byref(out))
+    assert st == 0 and out.value > 0 and out.value % 256 == 0
+    small = ctypes.c_size_t(0)
+    assert lib.dpg_project_workspace_size(_grads([(8, 8)]), 1, 1, 1, 1, 0,
+                                          ctypes.byref(small)) == 0
+    assert 0 < small.value < out.value
+    st = lib.dpg_adam_workspace_size(_params([(768, 3072)]), 1, 128, 1,
+                                     ctypes.byref(out))
+    assert st == 0 and out.value >= (768 + 3072) * 128 * 2
+
+
+BAD_PROJECT = [
+    # (description, overrides)
+    ("zero batch", dict(B=0)),
+    ("zero T", dict(T=0)),
+    ("zero r", dict(r=0)),
+    ("bad dtype", dict(dtype=7)),
+    ("zero layers", dict(n=0)),
+    ("negative C", dict(C=-1.0)),
+    ("zero C", dict(C=0.0)),
+    ("NaN C", dict(C=float("nan"))),
+    ("negative sigma", dict(sigma=-0.1)),
+    ("inf sigma", dict(sigma=float("inf"))),
+    ("inf C with noise", dict(C=float("inf"), sigma=1.0)),
+    ("step 0", dict(step=0)),
+    ("step 2^32", dict(step=2 ** 32)),
+    ("proj_step 2^32", dict(proj_step=2 ** 32)),
+    ("duplicate ids", dict(ids=[3, 3])),
+    ("zero d_in", dict(shapes=[(0, 4), (4, 4)])),
+    ("huge r*d", dict(shapes=[(2 ** 30, 4), (4, 4)], r=8)),
+    ("null data", dict(ptr=0)),
+]
+
+
+@pytest.mark.parametrize("desc,kw", BAD_PROJECT, ids=[d for d, _ in BAD_PROJECT])
+def test_project_rejects_invalid_arguments(lib, desc, kw):
+    shapes = kw.get("shapes", [(16, 8), (8, 16)])
+    arr = _grads(shapes, kw.get("ids"), kw.get("ptr", 0x1000))
+    st = lib.dpg_project_clip_noise(
+        arr, kw.get("n", len(shapes)), kw.get("B", 2), kw.get("T", 3),
+        kw.get("r", 4), kw.get("dtype", 1), kw.get("C", 1.0),
+        kw.get("sigma", 0.5), 0, kw.get("step", 1), kw.get("proj_step", 1),
+        None, 0x10000, 1 << 30, None)
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG, desc
+    assert lib.dpg_last_error() != b""
+
+
+def test_project_workspace_errors(lib):
+    arr = _grads([(16, 8)])
+    need = ctypes.c_size_t(0)
+    assert lib.dpg_project_workspace_size(arr, 1, 2, 3, 4, 1,
+                                          ctypes.byref(need)) == 0
+    args = (arr, 1, 2, 3, 4, 1, 1.0, 0.5, 0, 1, 1, None)
+    assert lib.dpg_project_clip_noise(*args, None, need.value, None) == 2
+    assert lib.dpg_project_clip_noise(*args, 0x10000, need.value - 1, None) == 2
+    assert lib.dpg_project_clip_noise(*args, 0x10010, need.value, None) == 2
+    assert b"workspace" in lib.dpg_last_error()
+
+
+BAD_ADAM = [
+    ("zero lr", dict(lr=0.0)),
+    ("inf lr", dict(lr=float("inf"))),
+    ("beta1 = 1", dict(b1=1.0)),
+    ("negative beta2", dict(b2=-0.1)),
+    ("zero eps", dict(eps=0.0)),
+    ("step 0", dict(step=0)),
+    ("zero r", dict(r=0)),
+    ("duplicate ids", dict(ids=[1, 1])),
+    ("null data", dict(ptr=0)),
+    ("bad dtype", dict(dtype=3)),
+]
+
+
+@pytest.mark.parametrize("desc,kw", BAD_ADAM, ids=[d for d, _ in BAD_ADAM])
+def test_adam_rejects_invalid_arguments(lib, desc, kw):
+    shapes = [(16, 8), (8, 16)]
+    arr = _params(shapes, kw.get("ids"), kw.get("ptr", 0x1000))
+    st = lib.dpg_adam_backproject(
+        arr, 2, kw.get("r", 4), kw.get("dtype", 1), kw.get("lr", 1e-3),
+        kw.get("b1", 0.9), kw.get("b2", 0.999), kw.get("eps", 1e-8), 0,
+        kw.get("step", 1), 1, 0x10000, 1 << 30, None)
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG, desc
+
+
+def test_philox_rejects_invalid_arguments(lib):
+    assert lib.dpg_philox_normals(0, 0, 0, 0, 0, 0, None, None, None) == 0
+    assert lib.dpg_philox_normals(0, 0, 0, 0, 0, 4, None, None, None) == 1
+    assert lib.dpg_philox_normals(0, 0, 0, 0, 2 ** 32 - 2, 4, 0x1000, None,
+                                  None) == 1
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        dpg.load_library(str(tmp_path / "missing.so"))
