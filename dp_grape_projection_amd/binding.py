@@ -74,16 +74,17 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     i32, i64, u32, u64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                           ctypes.c_uint64)
-    f32, vp, sz = ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.dpg_project_workspace_size.argtypes = [
         ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, ctypes.POINTER(sz)]
+    f64 = ctypes.c_double
     lib.dpg_project_clip_noise.argtypes = [
-        ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, f32, f32, u64,
+        ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, f64, f64, u64,
         u64, u64, vp, vp, sz, vp]
     lib.dpg_adam_workspace_size.argtypes = [
         ctypes.POINTER(LayerParam), i32, i32, i32, ctypes.POINTER(sz)]
     lib.dpg_adam_backproject.argtypes = [
-        ctypes.POINTER(LayerParam), i32, i32, i32, f32, f32, f32, f32, u64,
+        ctypes.POINTER(LayerParam), i32, i32, i32, f64, f64, f64, f64, u64,
         u64, u64, vp, sz, vp]
     lib.dpg_philox_normals.argtypes = [u64, u32, u32, u32, u64, u64, vp, vp, vp]
     for name in EXPORTED:

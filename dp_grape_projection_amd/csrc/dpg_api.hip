@@ -341,7 +341,7 @@ int dpg_adam_workspace_size(const dpg_layer_param* params, int32_t n_layers,
 
 int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
                            int64_t B, int64_t T, int32_t r, int32_t dtype,
-                           float clip_C, float sigma, uint64_t seed,
+                           double clip_C, double sigma, uint64_t seed,
                            uint64_t step, uint64_t proj_step,
                            float* sample_norms, void* workspace,
                            size_t workspace_bytes, void* stream) {
@@ -352,11 +352,11 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     if (!layers[i].A || !layers[i].dY || !layers[i].G_priv)
       return fail(DPG_ERR_INVALID_ARG,
                   "NULL data pointer in layer index " + std::to_string(i));
-  if (!(clip_C > 0.0f))
+  if (!(clip_C > 0.0))
     return fail(DPG_ERR_INVALID_ARG, "clip_C must be > 0");
-  if (!(sigma >= 0.0f) || std::isinf(sigma))
+  if (!(sigma >= 0.0) || std::isinf(sigma))
     return fail(DPG_ERR_INVALID_ARG, "sigma must be finite and >= 0");
-  if (std::isinf(clip_C) && sigma != 0.0f)
+  if (std::isinf(clip_C) && sigma != 0.0)
     return fail(DPG_ERR_INVALID_ARG, "sigma must be 0 when clip_C is infinite");
   if ((st = check_seed_steps(step, proj_step))) return st;
   const ProjPlan p = plan_proj(layers, n_layers, B, T, r, dtype);
@@ -448,14 +448,14 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     ScaleArgs a;
     a.norm_part = norm_part;
     a.n_slots = p.n_slots;
-    a.clip_C = clip_C;
+    a.clip_C = static_cast<float>(clip_C);
     a.scales = scales;
     a.norms_out = sample_norms;
     if ((st = timed(K_SCALE, s, [&] { return launch_scale(a, static_cast<int>(B), s); })))
       return st;
   }
   // 5-6. clipped sum over samples, then noise and 1/B
-  const double noise = sigma == 0.0f ? 0.0 : static_cast<double>(sigma) * clip_C;
+  const double noise = sigma == 0.0 ? 0.0 : sigma * clip_C;
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int l1 = std::min(n_layers, l0 + kMaxLayers);
     SampArgs a;
@@ -488,8 +488,8 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
 }
 
 int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
-                         int32_t r, int32_t dtype, float lr, float beta1,
-                         float beta2, float eps, uint64_t seed, uint64_t step,
+                         int32_t r, int32_t dtype, double lr, double beta1,
+                         double beta2, double eps, uint64_t seed, uint64_t step,
                          uint64_t proj_step, void* workspace,
                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
@@ -499,11 +499,11 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
     if (!params[i].G_priv || !params[i].W || !params[i].m || !params[i].v)
       return fail(DPG_ERR_INVALID_ARG,
                   "NULL data pointer in layer index " + std::to_string(i));
-  if (!(lr > 0.0f) || std::isinf(lr))
+  if (!(lr > 0.0) || std::isinf(lr))
     return fail(DPG_ERR_INVALID_ARG, "lr must be finite and > 0");
-  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
     return fail(DPG_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
-  if (!(eps > 0.0f) || std::isinf(eps))
+  if (!(eps > 0.0) || std::isinf(eps))
     return fail(DPG_ERR_INVALID_ARG, "eps must be finite and > 0");
   if ((st = check_seed_steps(step, proj_step))) return st;
   const AdamPlan p = plan_adam(params, n_layers, r, dtype);
@@ -520,13 +520,13 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
     std::memset(&a, 0, sizeof(a));
     a.r = r;
     a.ldr = static_cast<int32_t>(p.ldr);
-    a.beta1 = beta1;
-    a.beta2 = beta2;
-    a.one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(beta1));
-    a.one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(beta2));
-    a.bc1 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta1), t));
-    a.bc2 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta2), t));
-    a.eps = eps;
+    a.beta1 = static_cast<float>(beta1);
+    a.beta2 = static_cast<float>(beta2);
+    a.one_m_beta1 = static_cast<float>(1.0 - beta1);
+    a.one_m_beta2 = static_cast<float>(1.0 - beta2);
+    a.bc1 = static_cast<float>(1.0 - std::pow(beta1, t));
+    a.bc2 = static_cast<float>(1.0 - std::pow(beta2, t));
+    a.eps = static_cast<float>(eps);
     int blocks = 0;
     for (int l = l0; l < l1; ++l) {
       AdamLayer& L = a.L[l - l0];
@@ -552,7 +552,7 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
     std::memset(&b, 0, sizeof(b));
     b.r = r;
     b.ldr = static_cast<int32_t>(p.ldr);
-    b.lr = lr;
+    b.lr = static_cast<float>(lr);
     blocks = 0;
     for (int l = l0; l < l1; ++l) {
       BackLayer& L = b.L[l - l0];

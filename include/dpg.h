@@ -125,7 +125,7 @@ int dpg_project_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
  */
 int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
                            int64_t B, int64_t T, int32_t r, int32_t dtype,
-                           float clip_C, float sigma, uint64_t seed,
+                           double clip_C, double sigma, uint64_t seed,
                            uint64_t step, uint64_t proj_step,
                            float* sample_norms, void* workspace,
                            size_t workspace_bytes, void* stream);
@@ -149,11 +149,14 @@ int dpg_adam_workspace_size(const dpg_layer_param* params, int32_t n_layers,
  *     W <- W - lr P^T U          (P regenerated from seed, layer_id, proj_step)
  * Arguments: lr > 0 finite, 0 <= beta1, beta2 < 1, eps > 0, step >= 1
  * (< 2^32), proj_step as passed to dpg_project_clip_noise. m and v must be
- * zero before step 1. dtype selects the operand precision of P^T U.
+ * zero before step 1. dtype selects the operand precision of P^T U. The
+ * hyper-parameters are taken in double precision: 1 - beta and the bias
+ * corrections 1 - beta^t are formed in double before the kernels see them
+ * in fp32 (1 - beta2 from an fp32 beta2 = 0.999 would be off by 1e-5).
  */
 int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
-                         int32_t r, int32_t dtype, float lr, float beta1,
-                         float beta2, float eps, uint64_t seed, uint64_t step,
+                         int32_t r, int32_t dtype, double lr, double beta1,
+                         double beta2, double eps, uint64_t seed, uint64_t step,
                          uint64_t proj_step, void* workspace,
                          size_t workspace_bytes, void* stream);
 
