@@ -33,11 +33,11 @@ bool debug_sync() {
 }
 
 // ---- kernel-timing diagnostics (off unless dpg_timing_enable(1))
-enum Kind { K_GEN_P, K_PROJ, K_NORM, K_SCALE, K_SUM, K_FIN, K_ADAM, K_GEN_PT,
+enum Kind { K_GEN_P, K_PROJ, K_XSUM, K_NORM, K_SCALE, K_SUM, K_FIN, K_PREP,
             K_BACK, K_COUNT };
 static_assert(K_COUNT == DPG_N_KERNEL_KINDS, "kernel kinds");
-const char* const kKindName[K_COUNT] = {"gen_p", "proj", "norm", "scale", "sum",
-                                        "fin", "adam", "gen_pt", "back"};
+const char* const kKindName[K_COUNT] = {"gen_p", "proj", "xsum", "norm", "scale",
+                                        "sum", "fin", "prep", "back"};
 struct TimedLaunch {
   int kind;
   hipEvent_t start, stop;
@@ -124,13 +124,23 @@ int check_unique_ids(const L* layers, int32_t n) {
 
 // ------------------------------------------------ projection call planning --
 
+// Blocks resident at once that the split and grouping heuristics aim at: two
+// per compute unit of an MI355X (256 CUs), the occupancy the tiled kernels
+// run at (their register use allows two 256-thread blocks per CU).
+int64_t target_blocks(int32_t) { return 512; }
+
+int step_of(int32_t dtype) { return dtype == DPG_BF16 ? kStepBf16 : kStepF32; }
+
 struct ProjPlan {
   int64_t ldt = 0;             // row stride of Xt (T rounded up to 8)
   std::vector<int64_t> ldp;    // row stride of P per layer
-  std::vector<size_t> off_P, off_Xt, off_part;
-  std::vector<int32_t> m_tiles_proj, n_tiles_proj, m_tiles_s, n_tiles_s, slot0;
+  std::vector<size_t> off_P, off_Xt, off_part, off_xpart;
+  std::vector<int32_t> m_tiles, n_tiles_proj, splits, steps_per_split;
+  std::vector<int32_t> n_tiles_s, n_tiles_sum, slot0;
   int32_t n_slots = 0;
-  int32_t groups = 1, per_group = 1;
+  int32_t norm_per_block = 1;  // samples per norm block
+  int32_t groups = 1, per_group = 1;  // sum pass
+  bool fuse_scale = false;             // sum pass computes s_i itself
   size_t off_norm = 0, off_scales = 0, total = 0;
 };
 
@@ -149,7 +159,8 @@ int validate_proj_shapes(const dpg_layer_grad* layers, int32_t n_layers,
     if (st) return st;
     if (layers[i].reserved != 0)
       return fail(DPG_ERR_INVALID_ARG, "reserved field must be 0");
-    if (B * T * std::max(layers[i].d_in, layers[i].d_out) > (1ll << 46))
+    if (B * T * std::max(layers[i].d_in, layers[i].d_out) > (1ll << 46) ||
+        static_cast<int64_t>(r) * B * T > (1ll << 40))
       return fail(DPG_ERR_INVALID_ARG, "layer too large");
   }
   return check_unique_ids(layers, n_layers);
@@ -159,9 +170,19 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
                    int64_t T, int32_t r, int32_t dtype) {
   ProjPlan p;
   const size_t es = elem_size(dtype);
+  const int64_t BK = step_of(dtype);
+  const int64_t BT = B * T;
   p.ldt = round_up(T, 8);
+  const int32_t mt = static_cast<int32_t>(ceil_div(r, kTileM));
+  // Projection: K steps per block chosen so that about kTargetBlocks blocks
+  // share the work; a layer whose d_in needs more steps is split over d_in.
+  int64_t units = 0;
+  for (int l = 0; l < n_layers; ++l)
+    units += mt * ceil_div(BT, kTileN) * ceil_div(layers[l].d_in, BK);
+  const int64_t target = target_blocks(dtype);
+  const int64_t steps_per_block = std::max<int64_t>(1, ceil_div(units, target));
   size_t off = 0;
-  int64_t tiles_sum = 0;
+  int64_t tiles_s = 0, tiles_sum = 0;
   for (int l = 0; l < n_layers; ++l) {
     const int64_t ldp = round_up(layers[l].d_in, 8);
     p.ldp.push_back(ldp);
@@ -169,22 +190,53 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     off = align_up(off + static_cast<size_t>(r) * ldp * es);
     p.off_Xt.push_back(off);
     off = align_up(off + static_cast<size_t>(B) * r * p.ldt * es);
-    p.m_tiles_proj.push_back(static_cast<int32_t>(ceil_div(r, kProjBM)));
-    p.n_tiles_proj.push_back(static_cast<int32_t>(ceil_div(B * T, kProjBN)));
-    const int32_t mt = static_cast<int32_t>(ceil_div(r, kSampBM));
-    const int32_t nt = static_cast<int32_t>(ceil_div(layers[l].d_out, kSampBN));
-    p.m_tiles_s.push_back(mt);
+    const int64_t nsteps = ceil_div(layers[l].d_in, BK);
+    int64_t splits = ceil_div(nsteps, steps_per_block);
+    const int64_t sps = ceil_div(nsteps, splits);
+    splits = ceil_div(nsteps, sps);
+    p.m_tiles.push_back(mt);
+    p.n_tiles_proj.push_back(static_cast<int32_t>(ceil_div(BT, kTileN)));
+    p.splits.push_back(static_cast<int32_t>(splits));
+    p.steps_per_split.push_back(static_cast<int32_t>(sps));
+    p.off_xpart.push_back(off);
+    if (splits > 1) off = align_up(off + static_cast<size_t>(splits) * r * BT * 4);
+    const int32_t nt = static_cast<int32_t>(ceil_div(layers[l].d_out, kTileN));
     p.n_tiles_s.push_back(nt);
-    p.slot0.push_back(p.n_slots);
-    p.n_slots += mt * nt;
-    tiles_sum += static_cast<int64_t>(mt) * nt;
+    p.n_tiles_sum.push_back(static_cast<int32_t>(ceil_div(layers[l].d_out, kSumN)));
+    tiles_sum += static_cast<int64_t>(mt) * p.n_tiles_sum.back();
+    p.slot0.push_back(p.n_slots / 4);
+    p.n_slots += 4 * mt * nt;  // one partial per wave
+    tiles_s += static_cast<int64_t>(mt) * nt;
   }
-  // Sample groups of the second (sum) pass: enough blocks to cover the chip,
-  // each group adds one fp32 partial of G_priv.
-  int64_t groups = std::max<int64_t>(1, ceil_div(512, tiles_sum));
-  groups = std::min<int64_t>(groups, B);
-  p.per_group = static_cast<int32_t>(ceil_div(B, groups));
+  // Both per-sample passes give each block a run of samples of one tile. The
+  // run length is chosen to minimise (rounds of resident blocks) x (samples
+  // per block), so that the last round is not a small fraction of the chip.
+  // Norm pass: runs of up to 8 samples (ties: the longer run).
+  {
+    int64_t best = -1;
+    for (int64_t pb = 1; pb <= std::min<int64_t>(8, B); ++pb) {
+      const int64_t cost = ceil_div(tiles_s * ceil_div(B, pb), target) * pb;
+      if (best < 0 || cost <= best) {
+        best = cost;
+        p.norm_per_block = static_cast<int32_t>(pb);
+      }
+    }
+  }
+  // Sum pass: sample groups, each adding one fp32 partial of G_priv (ties:
+  // fewer groups, so fewer partials to add up).
+  {
+    int64_t best = -1;
+    for (int64_t per = B; per >= 1; --per) {
+      const int64_t g = ceil_div(B, per);
+      const int64_t cost = ceil_div(tiles_sum * g, target) * per;
+      if (best < 0 || cost < best) {
+        best = cost;
+        p.per_group = static_cast<int32_t>(per);
+      }
+    }
+  }
   p.groups = static_cast<int32_t>(ceil_div(B, p.per_group));
+  p.fuse_scale = p.per_group <= kFuseMaxGroup && p.n_slots <= kFuseMaxSlots;
   for (int l = 0; l < n_layers; ++l) {
     p.off_part.push_back(off);
     off = align_up(off + static_cast<size_t>(p.groups) * r * layers[l].d_out * 4);
@@ -200,8 +252,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
 // ---------------------------------------------------- update call planning --
 
 struct AdamPlan {
-  int64_t ldr = 0;
-  std::vector<size_t> off_Pt, off_Ut;
+  std::vector<size_t> off_P, off_U;
   size_t total = 0;
 };
 
@@ -225,13 +276,12 @@ AdamPlan plan_adam(const dpg_layer_param* params, int32_t n_layers, int32_t r,
                    int32_t dtype) {
   AdamPlan p;
   const size_t es = elem_size(dtype);
-  p.ldr = round_up(r, 8);
   size_t off = 0;
   for (int l = 0; l < n_layers; ++l) {
-    p.off_Pt.push_back(off);
-    off = align_up(off + static_cast<size_t>(params[l].d_in) * p.ldr * es);
-    p.off_Ut.push_back(off);
-    off = align_up(off + static_cast<size_t>(params[l].d_out) * p.ldr * es);
+    p.off_P.push_back(off);
+    off = align_up(off + static_cast<size_t>(params[l].d_in) * r * es);
+    p.off_U.push_back(off);
+    off = align_up(off + static_cast<size_t>(params[l].d_out) * r * es);
   }
   p.total = off;
   return p;
@@ -260,43 +310,16 @@ bool aligned(const void* p, size_t a) {
   return reinterpret_cast<uintptr_t>(p) % a == 0;
 }
 
-// Enqueue P generation for layers [l0, l1).
-template <class GetDin, class GetOut>
-int enqueue_gen_p(int l0, int l1, GetDin din, GetOut out_ld, uint32_t (*id)(int, const void*),
-                  const void* layers, int32_t r, uint64_t seed, uint32_t step_word,
-                  bool bf16, bool transposed, hipStream_t s) {
-  GenPArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.r = r;
-  a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(r)));
-  a.k0 = static_cast<uint32_t>(seed);
-  a.k1 = static_cast<uint32_t>(seed >> 32);
-  a.step_word = step_word;
-  int blocks = 0;
-  for (int l = l0; l < l1; ++l) {
-    GenPLayer& L = a.L[l - l0];
-    void* o;
-    int64_t ld;
-    out_ld(l, &o, &ld);
-    L.out = o;
-    L.ld = static_cast<int32_t>(ld);
-    L.d_in = static_cast<int32_t>(din(l));
-    L.layer_id = id(l, layers);
-    const uint64_t n = static_cast<uint64_t>(r) * L.d_in;
-    L.n_ctr = static_cast<int32_t>((n + 3) / 4);
-    L.block0 = blocks;
-    blocks += static_cast<int>(ceil_div(L.n_ctr, kThreads));
-  }
-  a.n_layers = l1 - l0;
-  return timed(transposed ? K_GEN_PT : K_GEN_P, s,
-               [&] { return launch_gen_p(a, blocks, bf16, transposed, s); });
-}
-
-uint32_t grad_id(int l, const void* p) {
-  return static_cast<const dpg_layer_grad*>(p)[l].layer_id;
-}
-uint32_t param_id(int l, const void* p) {
-  return static_cast<const dpg_layer_param*>(p)[l].layer_id;
+// Fills one P-generation descriptor; returns its number of blocks.
+int fill_gen_p(GenPLayer& L, void* out, int64_t d_in, int64_t ld,
+               uint32_t layer_id, int32_t r, int block0) {
+  L.out = out;
+  L.d_in = static_cast<int32_t>(d_in);
+  L.ld = static_cast<int32_t>(ld);
+  L.layer_id = layer_id;
+  L.n_ctr = static_cast<int32_t>((static_cast<uint64_t>(r) * d_in + 3) / 4);
+  L.block0 = block0;
+  return static_cast<int>(ceil_div(L.n_ctr, kThreads));
 }
 
 }  // namespace
@@ -365,58 +388,99 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = dtype == DPG_BF16;
-  const size_t es = elem_size(dtype);
-  const int vec_elems = static_cast<int>(16 / es);
+  const int vec_elems = static_cast<int>(16 / elem_size(dtype));
   float* norm_part = reinterpret_cast<float*>(ws + p.off_norm);
   float* scales = reinterpret_cast<float*>(ws + p.off_scales);
+  const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
+  const int64_t BT = B * T;
 
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int l1 = std::min(n_layers, l0 + kMaxLayers);
-    // 1. P_l, row-major [r][ldp]
-    st = enqueue_gen_p(
-        l0, l1, [&](int l) { return layers[l].d_in; },
-        [&](int l, void** o, int64_t* ld) { *o = ws + p.off_P[l]; *ld = p.ldp[l]; },
-        grad_id, layers, r, seed, static_cast<uint32_t>(proj_step), bf16, false, s);
-    if (st) return st;
-    // 2. Xt_l = P_l A_l^T, per sample [r][T]
+    // 1. P_l, row-major [r][ldp], regenerated from the seed
+    {
+      GenPArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.r = r;
+      a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(r)));
+      a.k0 = k0;
+      a.k1 = k1;
+      a.step_word = static_cast<uint32_t>(proj_step);
+      int blocks = 0;
+      for (int l = l0; l < l1; ++l)
+        blocks += fill_gen_p(a.L[l - l0], ws + p.off_P[l], layers[l].d_in,
+                             p.ldp[l], layers[l].layer_id, r, blocks);
+      a.n_layers = l1 - l0;
+      if ((st = timed(K_GEN_P, s, [&] { return launch_gen_p(a, blocks, bf16, s); })))
+        return st;
+    }
+    // 2. Xt_l = P_l A_l^T, per sample [r][T] (or split partials)
     ProjArgs a;
     std::memset(&a, 0, sizeof(a));
     a.B = static_cast<int32_t>(B);
     a.T = static_cast<int32_t>(T);
     a.r = r;
     a.ldt = static_cast<int32_t>(p.ldt);
-    int blocks = 0;
+    XsumArgs x;
+    std::memset(&x, 0, sizeof(x));
+    x.B = a.B;
+    x.T = a.T;
+    x.r = r;
+    x.ldt = a.ldt;
+    int blocks = 0, xblocks = 0, nx = 0;
     bool vec = true;
     for (int l = l0; l < l1; ++l) {
       ProjLayer& L = a.L[l - l0];
       L.A = layers[l].A;
       L.P = ws + p.off_P[l];
       L.Xt = ws + p.off_Xt[l];
+      L.part = reinterpret_cast<float*>(ws + p.off_xpart[l]);
       L.d_in = static_cast<int32_t>(layers[l].d_in);
       L.ldp = static_cast<int32_t>(p.ldp[l]);
-      L.m_tiles = p.m_tiles_proj[l];
+      L.m_tiles = p.m_tiles[l];
       L.n_tiles = p.n_tiles_proj[l];
+      L.splits = p.splits[l];
+      L.steps_per_split = p.steps_per_split[l];
       L.block0 = blocks;
-      blocks += L.m_tiles * L.n_tiles;
+      blocks += L.m_tiles * L.n_tiles * L.splits;
       vec = vec && layers[l].d_in % vec_elems == 0 && aligned(layers[l].A, 16);
+      if (L.splits > 1) {
+        XsumLayer& X = x.L[nx++];
+        X.part = L.part;
+        X.Xt = L.Xt;
+        X.splits = L.splits;
+        X.block0 = xblocks;
+        xblocks += static_cast<int>(ceil_div(ceil_div(BT, 4) * r, kThreads));
+      }
     }
     a.n_layers = l1 - l0;
     a.n_blocks = blocks;
+    // 32-bit tile offsets: 128 rows of A or of P (row stride ldp)
+    a.off32 = 1;
+    for (int l = l0; l < l1; ++l)
+      if (static_cast<uint64_t>(kTileN) * p.ldp[l] * elem_size(dtype) >= (1ull << 31))
+        a.off32 = 0;
     if ((st = timed(K_PROJ, s, [&] { return launch_proj(a, bf16, vec, s); }))) return st;
+    if (nx > 0) {
+      x.n_layers = nx;
+      if ((st = timed(K_XSUM, s, [&] { return launch_xsum(x, xblocks, bf16, s); })))
+        return st;
+    }
   }
 
-  // 3. squared-norm partials of every (sample, layer, tile)
   auto fill_samp = [&](SampArgs& a, int l0, int l1, bool sum, bool* pair) {
     std::memset(&a, 0, sizeof(a));
     a.B = static_cast<int32_t>(B);
     a.T = static_cast<int32_t>(T);
     a.r = r;
     a.ldt = static_cast<int32_t>(p.ldt);
-    a.groups = p.groups;
-    a.per_group = p.per_group;
+    a.per_block = sum ? p.per_group : p.norm_per_block;
     a.n_slots = p.n_slots;
     a.norm_part = norm_part;
     a.scales = scales;
+    a.fuse_scale = sum && p.fuse_scale;
+    a.clip_C = static_cast<float>(clip_C);
+    a.norms_out = (sum && p.fuse_scale && l0 == 0) ? sample_norms : nullptr;
+    const int64_t runs = ceil_div(B, a.per_block);
     int blocks = 0;
     *pair = true;
     for (int l = l0; l < l1; ++l) {
@@ -425,16 +489,23 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
       L.Xt = ws + p.off_Xt[l];
       L.part = reinterpret_cast<float*>(ws + p.off_part[l]);
       L.d_out = static_cast<int32_t>(layers[l].d_out);
-      L.m_tiles = p.m_tiles_s[l];
-      L.n_tiles = p.n_tiles_s[l];
+      L.m_tiles = p.m_tiles[l];
+      L.n_tiles = sum ? p.n_tiles_sum[l] : p.n_tiles_s[l];
       L.slot0 = p.slot0[l];
       L.block0 = blocks;
-      blocks += L.m_tiles * L.n_tiles * (sum ? p.groups : static_cast<int32_t>(B));
+      blocks += static_cast<int>(L.m_tiles * L.n_tiles * runs);
+      // bf16: dY is gathered two columns (4 bytes) at a time
       *pair = *pair && layers[l].d_out % 2 == 0 && aligned(layers[l].dY, 4);
     }
     a.n_layers = l1 - l0;
     a.n_blocks = blocks;
+    // 32-bit tile offsets: one sample of dY, and 128 rows of Xt
+    a.off32 = static_cast<uint64_t>(kTileM) * p.ldt * elem_size(dtype) < (1ull << 31);
+    for (int l = l0; l < l1; ++l)
+      if (static_cast<uint64_t>(T) * layers[l].d_out * elem_size(dtype) >= (1ull << 31))
+        a.off32 = 0;
   };
+  // 3. squared-norm partials of every (sample, layer, tile)
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int l1 = std::min(n_layers, l0 + kMaxLayers);
     SampArgs a;
@@ -443,8 +514,9 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     if ((st = timed(K_NORM, s, [&] { return launch_samp_norm(a, bf16, pair, s); })))
       return st;
   }
-  // 4. per-sample norm and clip factor (needs every layer's partials)
-  {
+  // 4. per-sample norm and clip factor (needs every layer's partials); the
+  //    sum pass does it itself when the groups are small
+  if (!p.fuse_scale) {
     ScaleArgs a;
     a.norm_part = norm_part;
     a.n_slots = p.n_slots;
@@ -468,8 +540,8 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     f.groups = p.groups;
     f.noise_scale = static_cast<float>(noise);
     f.inv_B = static_cast<float>(1.0 / static_cast<double>(B));
-    f.k0 = static_cast<uint32_t>(seed);
-    f.k1 = static_cast<uint32_t>(seed >> 32);
+    f.k0 = k0;
+    f.k1 = k1;
     f.step_word = static_cast<uint32_t>(step);
     int blocks = 0;
     for (int l = l0; l < l1; ++l) {
@@ -515,11 +587,10 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
   const double t = static_cast<double>(step);
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int l1 = std::min(n_layers, l0 + kMaxLayers);
-    // 5. Adam on [r][d_out]; U written transposed for the back-projection
-    AdamArgs a;
+    // 5. Adam on [r][d_out] (U row-major) and P_l regenerated [r][d_in]
+    PrepArgs a;
     std::memset(&a, 0, sizeof(a));
     a.r = r;
-    a.ldr = static_cast<int32_t>(p.ldr);
     a.beta1 = static_cast<float>(beta1);
     a.beta2 = static_cast<float>(beta2);
     a.one_m_beta1 = static_cast<float>(1.0 - beta1);
@@ -527,48 +598,58 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
     a.bc1 = static_cast<float>(1.0 - std::pow(beta1, t));
     a.bc2 = static_cast<float>(1.0 - std::pow(beta2, t));
     a.eps = static_cast<float>(eps);
+    a.p_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(r)));
+    a.k0 = static_cast<uint32_t>(seed);
+    a.k1 = static_cast<uint32_t>(seed >> 32);
+    a.step_word = static_cast<uint32_t>(proj_step);
     int blocks = 0;
     for (int l = l0; l < l1; ++l) {
-      AdamLayer& L = a.L[l - l0];
+      AdamLayer& L = a.A[l - l0];
       L.g = params[l].G_priv;
       L.m = params[l].m;
       L.v = params[l].v;
-      L.Ut = ws + p.off_Ut[l];
-      L.d_out = static_cast<int32_t>(params[l].d_out);
+      L.U = ws + p.off_U[l];
       L.n_elem = static_cast<int32_t>(static_cast<int64_t>(r) * params[l].d_out);
       L.block0 = blocks;
       blocks += static_cast<int>(ceil_div(ceil_div(L.n_elem, 4), kThreads));
     }
+    a.adam_blocks = blocks;
+    int pblocks = 0;
+    for (int l = l0; l < l1; ++l)
+      pblocks += fill_gen_p(a.P[l - l0], ws + p.off_P[l], params[l].d_in,
+                            params[l].d_in, params[l].layer_id, r, pblocks);
     a.n_layers = l1 - l0;
-    if ((st = timed(K_ADAM, s, [&] { return launch_adam(a, blocks, bf16, s); }))) return st;
-    // P_l regenerated, transposed [d_in][ldr]
-    st = enqueue_gen_p(
-        l0, l1, [&](int l) { return params[l].d_in; },
-        [&](int l, void** o, int64_t* ld) { *o = ws + p.off_Pt[l]; *ld = p.ldr; },
-        param_id, params, r, seed, static_cast<uint32_t>(proj_step), bf16, true, s);
-    if (st) return st;
+    if ((st = timed(K_PREP, s, [&] { return launch_prep(a, blocks + pblocks, bf16, s); })))
+      return st;
     // 6. W -= lr P^T U
     BackArgs b;
     std::memset(&b, 0, sizeof(b));
     b.r = r;
-    b.ldr = static_cast<int32_t>(p.ldr);
     b.lr = static_cast<float>(lr);
     blocks = 0;
+    bool pair = true;
     for (int l = l0; l < l1; ++l) {
       BackLayer& L = b.L[l - l0];
-      L.Pt = ws + p.off_Pt[l];
-      L.Ut = ws + p.off_Ut[l];
+      L.P = ws + p.off_P[l];
+      L.U = ws + p.off_U[l];
       L.W = params[l].W;
       L.d_in = static_cast<int32_t>(params[l].d_in);
       L.d_out = static_cast<int32_t>(params[l].d_out);
-      L.m_tiles = static_cast<int32_t>(ceil_div(params[l].d_in, kBackBM));
-      L.n_tiles = static_cast<int32_t>(ceil_div(params[l].d_out, kBackBN));
+      L.m_tiles = static_cast<int32_t>(ceil_div(params[l].d_in, kTileM));
+      L.n_tiles = static_cast<int32_t>(ceil_div(params[l].d_out, kBackN));
       L.block0 = blocks;
       blocks += L.m_tiles * L.n_tiles;
+      // bf16: P and U are gathered two columns (4 bytes) at a time
+      pair = pair && params[l].d_in % 2 == 0 && params[l].d_out % 2 == 0;
     }
     b.n_layers = l1 - l0;
     b.n_blocks = blocks;
-    if ((st = timed(K_BACK, s, [&] { return launch_back(b, bf16, s); }))) return st;
+    b.off32 = 1;
+    for (int l = l0; l < l1; ++l)
+      if (static_cast<uint64_t>(r) * std::max(params[l].d_in, params[l].d_out) *
+              elem_size(dtype) >= (1ull << 31))
+        b.off32 = 0;
+    if ((st = timed(K_BACK, s, [&] { return launch_back(b, bf16, pair, s); }))) return st;
   }
   return DPG_OK;
 }

@@ -107,27 +107,55 @@ template <typename T> __device__ __forceinline__ T zero_val() { return from_floa
 
 // ----------------------------------------------------------- tile engine --
 //
-// A block computes C[BM x BN] = sum_k Aop[m][k] * Bop[n][k] with both operands
-// staged in LDS as K-contiguous rows (sA[m][k], sB[n][k]). The four waves
-// split the tile 2 x 2; wave w owns rows [(w & 1) * BM/2, +BM/2) and columns
-// [(w >> 1) * BN/2, +BN/2) as MB x NB blocks of 32 x 32.
+// A block of 4 waves computes C[BM x BN] = sum_k Aop[m][k] * Bop[n][k] with
+// both operands staged in LDS as K-contiguous rows (sA[m][k], sB[n][k]). The
+// waves are laid out WGM x WGN over the tile; each owns a WTM x WTN wave tile
+// of MB x NB blocks of 32 x 32 computed with the 32x32 matrix-core
+// instructions (fp32 accumulation).
 //
-// Accumulator layout of a 32x32 block (v_mfma_f32_32x32x*): lane l holds
-// column (l & 31) and, in register i = 0..15, row 8*(i/4) + 4*(l >> 5) + (i & 3).
+// Accumulator layout of one 32x32 block: lane l, register i = 0..15 holds row
+// 8*(i/4) + 4*(l >> 5) + (i & 3) and column (l & 31) of the block.
+//
+// Columns are interleaved across the NB blocks of a wave tile: LDS row
+// nb*32 + q of the wave tile holds operand column NB*q + nb. Block nb's
+// column q is therefore tile column NB*q + nb, and every lane owns NB
+// consecutive output columns of each of its rows, so epilogues read and write
+// NB-wide vectors.
 
-template <typename T, int BK>
-struct LdsRow {
-  static constexpr int kPad = 16 / sizeof(T);  // 16-byte pad per row
-  static constexpr int kStride = BK + kPad;    // elements per LDS row
+template <typename T, int BM_, int BN_, int BK_, int WGM_, int WGN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+  static_assert(WGM * WGN == 4, "4 waves per block");
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int MB = WTM / 32, NB = WTN / 32;
+  static_assert(MB >= 1 && NB >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
+  static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+  static constexpr int S = BK + 16 / static_cast<int>(sizeof(T));  // LDS row stride
+  static constexpr int kLdsElems = (BM + BN) * S;
+
+  __device__ __forceinline__ static int wave_m(int wave) { return wave % WGM; }
+  __device__ __forceinline__ static int wave_n(int wave) { return wave / WGM; }
+  // LDS row that holds B-operand column c of the tile.
+  __device__ __forceinline__ static int b_row(int c) {
+    const int wn = c / WTN, cl = c - wn * WTN;
+    return wn * WTN + (cl % NB) * 32 + cl / NB;
+  }
+  // Tile row of accumulator register i of block mb.
+  __device__ __forceinline__ static int acc_row(int wm, int mb, int i, int lane) {
+    return wm * WTM + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+  }
+  // Tile column of block nb in this lane.
+  __device__ __forceinline__ static int acc_col(int wn, int nb, int lane) {
+    return wn * WTN + NB * (lane & 31) + nb;
+  }
 };
 
-template <typename T, int BM, int BN, int BK>
-struct TileShape {
-  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
-  static constexpr int MB = WTM / 32, NB = WTN / 32;
-  static constexpr int S = LdsRow<T, BK>::kStride;
-  static_assert(MB >= 1 && NB >= 1, "tile too small");
-  static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+struct IdentityRows {
+  __device__ __forceinline__ static int map(int c) { return c; }
+};
+template <class Tl>
+struct BOperandRows {
+  __device__ __forceinline__ static int map(int c) { return Tl::b_row(c); }
 };
 
 template <int MB, int NB>
@@ -141,59 +169,75 @@ struct Acc {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[a][b][i] = 0.0f;
   }
+  __device__ __forceinline__ void fma_from(float s, const Acc& o) {
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[a][b][i] = fmaf(s, o.v[a][b][i], v[a][b][i]);
+  }
+  __device__ __forceinline__ float sum_sq() const {
+    float s = 0.0f;
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = fmaf(v[a][b][i], v[a][b][i], s);
+    return s;
+  }
 };
 
 // One BK-deep step of matrix-core work from LDS.
-template <typename T, int BM, int BN, int BK> struct Mma;
+template <typename T, class Tl> struct Mma;
 
-template <int BM, int BN, int BK>
-struct Mma<bf16, BM, BN, BK> {
-  typedef TileShape<bf16, BM, BN, BK> Sh;
+template <class Tl>
+struct Mma<bf16, Tl> {
   __device__ __forceinline__ static void run(const bf16* sA, const bf16* sB,
-                                             Acc<Sh::MB, Sh::NB>& acc, int wm,
+                                             Acc<Tl::MB, Tl::NB>& acc, int wm,
                                              int wn, int lane) {
     const int r = lane & 31, kq = (lane >> 5) * 8;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 a[Sh::MB], b[Sh::NB];
+    for (int kk = 0; kk < Tl::BK; kk += 16) {
+      bf16x8 a[Tl::MB], b[Tl::NB];
 #pragma unroll
-      for (int mb = 0; mb < Sh::MB; ++mb)
+      for (int mb = 0; mb < Tl::MB; ++mb)
         a[mb] = *reinterpret_cast<const bf16x8*>(
-            sA + (wm * Sh::WTM + mb * 32 + r) * Sh::S + kk + kq);
+            sA + (wm * Tl::WTM + mb * 32 + r) * Tl::S + kk + kq);
 #pragma unroll
-      for (int nb = 0; nb < Sh::NB; ++nb)
+      for (int nb = 0; nb < Tl::NB; ++nb)
         b[nb] = *reinterpret_cast<const bf16x8*>(
-            sB + (wn * Sh::WTN + nb * 32 + r) * Sh::S + kk + kq);
+            sB + (wn * Tl::WTN + nb * 32 + r) * Tl::S + kk + kq);
 #pragma unroll
-      for (int mb = 0; mb < Sh::MB; ++mb)
+      for (int mb = 0; mb < Tl::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < Sh::NB; ++nb)
+        for (int nb = 0; nb < Tl::NB; ++nb)
           acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               a[mb], b[nb], acc.v[mb][nb], 0, 0, 0);
     }
   }
 };
 
-template <int BM, int BN, int BK>
-struct Mma<float, BM, BN, BK> {
-  typedef TileShape<float, BM, BN, BK> Sh;
+template <class Tl>
+struct Mma<float, Tl> {
   __device__ __forceinline__ static void run(const float* sA, const float* sB,
-                                             Acc<Sh::MB, Sh::NB>& acc, int wm,
+                                             Acc<Tl::MB, Tl::NB>& acc, int wm,
                                              int wn, int lane) {
     const int r = lane & 31, kq = lane >> 5;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      float a[Sh::MB], b[Sh::NB];
+    for (int kk = 0; kk < Tl::BK; kk += 2) {
+      float a[Tl::MB], b[Tl::NB];
 #pragma unroll
-      for (int mb = 0; mb < Sh::MB; ++mb)
-        a[mb] = sA[(wm * Sh::WTM + mb * 32 + r) * Sh::S + kk + kq];
+      for (int mb = 0; mb < Tl::MB; ++mb)
+        a[mb] = sA[(wm * Tl::WTM + mb * 32 + r) * Tl::S + kk + kq];
 #pragma unroll
-      for (int nb = 0; nb < Sh::NB; ++nb)
-        b[nb] = sB[(wn * Sh::WTN + nb * 32 + r) * Sh::S + kk + kq];
+      for (int nb = 0; nb < Tl::NB; ++nb)
+        b[nb] = sB[(wn * Tl::WTN + nb * 32 + r) * Tl::S + kk + kq];
 #pragma unroll
-      for (int mb = 0; mb < Sh::MB; ++mb)
+      for (int mb = 0; mb < Tl::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < Sh::NB; ++nb)
+        for (int nb = 0; nb < Tl::NB; ++nb)
           acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
               a[mb], b[nb], acc.v[mb][nb], 0, 0, 0);
     }
@@ -201,25 +245,38 @@ struct Mma<float, BM, BN, BK> {
 };
 
 // Loads ROWS x BK of a K-contiguous source (row stride ld elements; rows
-// >= nrows and columns >= K read as zero) into registers, then into LDS
-// sX[row][k]. VEC: 16-byte loads (needs ld % (16/sizeof(T)) == 0 and a
-// 16-byte aligned base); otherwise element loads.
-template <typename T, int ROWS, int BK, bool VEC>
+// >= nrows and columns >= K read as zero) into registers, then stores source
+// row c into LDS row Map::map(c). VEC: 16-byte loads (needs ld % (16 /
+// sizeof(T)) == 0 and a 16-byte aligned base); otherwise element loads.
+template <typename T, int ROWS, int BK, bool VEC, class Map>
 struct RowsLoader {
   typedef typename Vec16<T>::type V;
   static constexpr int VN = Vec16<T>::N;
-  static constexpr int CPR = BK / VN;               // chunks per row
-  static constexpr int PER = ROWS * CPR / kThreads; // chunks per thread
+  static constexpr int CPR = BK / VN;                // chunks per row
+  static constexpr int PER = ROWS * CPR / kThreads;  // chunks per thread
   static_assert(PER >= 1 && (ROWS * CPR) % kThreads == 0, "bad tiling");
-  static constexpr int S = LdsRow<T, BK>::kStride;
+  static constexpr int S = BK + VN;
 
-  const T* base;
   int64_t ld;
   int nrows;
   int K;
   V reg[PER];
 
-  __device__ __forceinline__ void load(int k0, int tid) {
+  // off32: every byte offset of the tile from `base` fits in 32 bits (lets
+  // a full tile use block-uniform base + 32-bit lane offset addressing).
+  __device__ __forceinline__ void load(const T* base, int k0, int tid,
+                                       bool off32) {
+    if (VEC && off32 && nrows >= ROWS && k0 + BK <= K) {
+      const char* bb = reinterpret_cast<const char*>(base);
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int ci = tid + p * kThreads;
+        const uint32_t off = (static_cast<uint32_t>(ci / CPR) * static_cast<uint32_t>(ld) +
+                              static_cast<uint32_t>(k0 + (ci % CPR) * VN)) * sizeof(T);
+        reg[p] = *reinterpret_cast<const V*>(bb + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int ci = tid + p * kThreads;
@@ -251,7 +308,7 @@ struct RowsLoader {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int ci = tid + p * kThreads;
-      const int row = ci / CPR;
+      const int row = Map::map(ci / CPR);
       const int kc = (ci % CPR) * VN;
       *reinterpret_cast<V*>(sX + row * S + kc) = reg[p];
     }
@@ -259,28 +316,44 @@ struct RowsLoader {
 };
 
 // Loads BK x COLS of an N-contiguous source X[k][n] (row stride ld) and
-// stores it transposed into LDS sX[n][k], so that the contraction index k
-// ends up contiguous for the matrix cores. Rows >= K and columns >= ncols
-// read as zero. Each thread gathers 8 consecutive k of one or two columns.
-template <typename T, int COLS, int BK, bool PAIR>
+// stores it transposed into LDS (column c -> LDS row Map::map(c), k
+// contiguous), so that the contraction index ends up contiguous for the
+// matrix cores. Rows >= K and columns >= ncols read as zero. Each thread
+// gathers 8 consecutive k of one or two columns.
+template <typename T, int COLS, int BK, bool PAIR, class Map>
 struct ColsLoader;
 
-// bf16, PAIR: a thread loads 32-bit words (2 columns) from 8 consecutive
-// rows and splits them into two 8-element k-vectors (needs an even ld, an
-// even column offset and a 4-byte aligned base).
-template <int COLS, int BK>
-struct ColsLoader<bf16, COLS, BK, true> {
-  static constexpr int S = LdsRow<bf16, BK>::kStride;
+// bf16, PAIR: 32-bit loads (2 columns) from 8 consecutive rows, split into
+// two 8-element k-vectors (needs an even ld, an even column offset of the
+// base and a 4-byte aligned base).
+template <int COLS, int BK, class Map>
+struct ColsLoader<bf16, COLS, BK, true, Map> {
+  static constexpr int S = BK + 8;
   static constexpr int ITEMS = (COLS / 2) * (BK / 8);
   static constexpr int PER = ITEMS / kThreads;
   static_assert(PER >= 1 && ITEMS % kThreads == 0, "bad tiling");
-  const bf16* base;
   int64_t ld;
   int ncols;
   int K;
   uint32_t w[PER][8];
 
-  __device__ __forceinline__ void load(int k0, int tid) {
+  __device__ __forceinline__ void load(const bf16* base, int k0, int tid,
+                                       bool off32) {
+    if (off32 && ncols >= COLS && k0 + BK <= K) {
+      const char* bb = reinterpret_cast<const char*>(base);
+      const uint32_t stride = static_cast<uint32_t>(ld) * 2u;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int it = tid + p * kThreads;
+        const uint32_t c = (it % (COLS / 2)) * 2;
+        const uint32_t k = k0 + (it / (COLS / 2)) * 8;
+        const uint32_t off = k * stride + c * 2u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          w[p][j] = *reinterpret_cast<const uint32_t*>(bb + off + j * stride);
+      }
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int it = tid + p * kThreads;
@@ -315,38 +388,42 @@ struct ColsLoader<bf16, COLS, BK, true> {
         lo[j] = (a & 0xFFFFu) | (b << 16);
         hi[j] = (a >> 16) | (b & 0xFFFF0000u);
       }
-      *reinterpret_cast<u32x4*>(sX + c * S + kc) = lo;
-      *reinterpret_cast<u32x4*>(sX + (c + 1) * S + kc) = hi;
+      *reinterpret_cast<u32x4*>(sX + Map::map(c) * S + kc) = lo;
+      *reinterpret_cast<u32x4*>(sX + Map::map(c + 1) * S + kc) = hi;
     }
   }
 };
 
 // bf16, element loads (odd row stride or unaligned base).
-template <int COLS, int BK>
-struct ColsLoader<bf16, COLS, BK, false> {
-  static constexpr int S = LdsRow<bf16, BK>::kStride;
+template <int COLS, int BK, class Map>
+struct ColsLoader<bf16, COLS, BK, false, Map> {
+  static constexpr int S = BK + 8;
   static constexpr int ITEMS = COLS * (BK / 8);
   static constexpr int PER = ITEMS / kThreads;
   static_assert(PER >= 1 && ITEMS % kThreads == 0, "bad tiling");
-  const bf16* base;
   int64_t ld;
   int ncols;
   int K;
-  uint16_t h[PER][8];
+  uint32_t h[PER][4];  // 8 bf16 packed in pairs
 
-  __device__ __forceinline__ void load(int k0, int tid) {
+  __device__ __forceinline__ void load(const bf16* base, int k0, int tid, bool) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int it = tid + p * kThreads;
       const int c = it % COLS;
       const int k = k0 + (it / COLS) * 8;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint16_t x = 0;
-        if (k + j < K && c < ncols)
-          x = *reinterpret_cast<const uint16_t*>(
-              base + static_cast<int64_t>(k + j) * ld + c);
-        h[p][j] = x;
+      for (int j = 0; j < 8; j += 2) {
+        uint32_t lo = 0, hi = 0;
+        if (c < ncols) {
+          if (k + j < K)
+            lo = *reinterpret_cast<const uint16_t*>(
+                base + static_cast<int64_t>(k + j) * ld + c);
+          if (k + j + 1 < K)
+            hi = *reinterpret_cast<const uint16_t*>(
+                base + static_cast<int64_t>(k + j + 1) * ld + c);
+        }
+        h[p][j / 2] = lo | (hi << 16);
       }
     }
   }
@@ -359,29 +436,26 @@ struct ColsLoader<bf16, COLS, BK, false> {
       const int kc = (it / COLS) * 8;
       u32x4 v;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        v[j] = static_cast<uint32_t>(h[p][2 * j]) |
-               (static_cast<uint32_t>(h[p][2 * j + 1]) << 16);
-      *reinterpret_cast<u32x4*>(sX + c * S + kc) = v;
+      for (int j = 0; j < 4; ++j) v[j] = h[p][j];
+      *reinterpret_cast<u32x4*>(sX + Map::map(c) * S + kc) = v;
     }
   }
 };
 
 // fp32: a thread loads one column from 4 consecutive rows (4-byte loads,
 // consecutive lanes on consecutive columns) and stores one 16-byte k-vector.
-template <int COLS, int BK, bool PAIR>
-struct ColsLoader<float, COLS, BK, PAIR> {
-  static constexpr int S = LdsRow<float, BK>::kStride;
+template <int COLS, int BK, bool PAIR, class Map>
+struct ColsLoader<float, COLS, BK, PAIR, Map> {
+  static constexpr int S = BK + 4;
   static constexpr int ITEMS = COLS * (BK / 4);
   static constexpr int PER = ITEMS / kThreads;
   static_assert(PER >= 1 && ITEMS % kThreads == 0, "bad tiling");
-  const float* base;
   int64_t ld;
   int ncols;
   int K;
   f32x4 reg[PER];
 
-  __device__ __forceinline__ void load(int k0, int tid) {
+  __device__ __forceinline__ void load(const float* base, int k0, int tid, bool) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int it = tid + p * kThreads;
@@ -403,44 +477,35 @@ struct ColsLoader<float, COLS, BK, PAIR> {
       const int it = tid + p * kThreads;
       const int c = it % COLS;
       const int kc = (it / COLS) * 4;
-      *reinterpret_cast<f32x4*>(sX + c * S + kc) = reg[p];
+      *reinterpret_cast<f32x4*>(sX + Map::map(c) * S + kc) = reg[p];
     }
   }
 };
 
-// Runs the K loop [k_begin, k_end) in BK steps: the next step's global loads
-// are issued before the current step's matrix-core work.
-template <typename T, int BM, int BN, int BK, class LA, class LB>
-__device__ __forceinline__ void k_loop(LA& la, LB& lb, T* sA, T* sB,
-                                       Acc<TileShape<T, BM, BN, BK>::MB,
-                                           TileShape<T, BM, BN, BK>::NB>& acc,
-                                       int k_begin, int k_end, int tid) {
+// Runs n_steps BK-deep steps. load_step(s) issues the global loads of step s
+// into the loaders' registers; the loads of step s + 1 are in flight while
+// step s runs on the matrix cores. after_step(s) runs once step s has been
+// accumulated.
+template <typename T, class Tl, class LA, class LB, class LoadStep, class AfterStep>
+__device__ __forceinline__ void run_steps(LA& la, LB& lb, T* smem,
+                                          Acc<Tl::MB, Tl::NB>& acc, int n_steps,
+                                          int tid, LoadStep load_step,
+                                          AfterStep after_step) {
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  if (k_begin >= k_end) return;
-  la.load(k_begin, tid);
-  lb.load(k_begin, tid);
-  for (int k0 = k_begin; k0 < k_end; k0 += BK) {
-    __syncthreads();  // previous step finished reading LDS
+  const int wm = Tl::wave_m(wave), wn = Tl::wave_n(wave);
+  T* sA = smem;
+  T* sB = smem + Tl::BM * Tl::S;
+  if (n_steps <= 0) return;
+  load_step(0);
+  for (int s = 0; s < n_steps; ++s) {
+    __syncthreads();  // the previous step finished reading LDS
     la.store(sA, tid);
     lb.store(sB, tid);
     __syncthreads();
-    if (k0 + BK < k_end) {
-      la.load(k0 + BK, tid);
-      lb.load(k0 + BK, tid);
-    }
-    Mma<T, BM, BN, BK>::run(sA, sB, acc, wm, wn, lane);
+    if (s + 1 < n_steps) load_step(s + 1);
+    Mma<T, Tl>::run(sA, sB, acc, wm, wn, lane);
+    after_step(s);
   }
-}
-
-// Row (within the block tile) of accumulator register i of block (mb, .).
-template <int WTM>
-__device__ __forceinline__ int acc_row(int wm, int mb, int i, int lane) {
-  return wm * WTM + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
-template <int WTN>
-__device__ __forceinline__ int acc_col(int wn, int nb, int lane) {
-  return wn * WTN + nb * 32 + (lane & 31);
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).

@@ -12,16 +12,21 @@ namespace dpg {
 constexpr int kThreads = 256;  // every kernel: 4 wavefronts of 64 lanes
 constexpr int kMaxLayers = 32;
 
-// Tile sizes (rows x cols x k) of the matrix-core kernels.
-constexpr int kProjBM = 128, kProjBN = 64, kProjBK = 32;     // Xt = P A^T
-constexpr int kSampBM = 128, kSampBN = 128, kSampBK = 32;    // Xt_i dY_i
-constexpr int kBackBM = 128, kBackBN = 128, kBackBK = 32;    // P^T U
+// Matrix-core tiles: 128 x 128 outputs per block; the K step is 128 for
+// bf16 operands and 32 for fp32 operands.
+constexpr int kTileM = 128, kTileN = 128;
+constexpr int kBackN = 64;  // back-projection: 128 x 64 output tiles
+constexpr int kSumN = 64;   // clipped-sum pass: 128 x 64 output tiles
+// The sum pass folds the per-sample norm and clip factor into its prologue
+// when a group holds at most this many samples and each sample at most this
+// many norm partials.
+constexpr int kFuseMaxGroup = 64, kFuseMaxSlots = 1024;
+constexpr int kStepBf16 = 128, kStepF32 = 32;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
 
-// ---- P generation (row-major [r][ld] for the projection, or transposed
-//      [d_in][ld] for the back-projection)
+// ---- P generation: P[j][k] = z / sqrt(r), row-major with row stride ld
 struct GenPLayer {
   void* out;
   int32_t d_in;
@@ -39,15 +44,20 @@ struct GenPArgs {
   uint32_t k0, k1, step_word;
 };
 
-// ---- Xt = P A^T, written per sample as Xt[b][j][t] (row stride ldt)
+// ---- Xt = P A^T over a K range; written per sample as Xt[b][j][t] (row
+//      stride ldt) when the layer is not split, else as an fp32 partial
+//      part[split][j][n] (n = b*T + t) summed afterwards by the xsum kernel
 struct ProjLayer {
   const void* A;      // [B*T][d_in]
   const void* P;      // [r][ldp]
   void* Xt;           // [B][r][ldt]
+  float* part;        // [splits][r][B*T] when splits > 1
   int32_t d_in;
   int32_t ldp;
   int32_t m_tiles;    // over r
   int32_t n_tiles;    // over B*T
+  int32_t splits;     // K ranges
+  int32_t steps_per_split;
   int32_t block0;
   int32_t pad;
 };
@@ -55,6 +65,19 @@ struct ProjArgs {
   ProjLayer L[kMaxLayers];
   int32_t n_layers;
   int32_t n_blocks;   // logical blocks (grid is rounded up to a multiple of 8)
+  int32_t B, T, r, ldt;
+  int32_t off32;      // activation tiles addressable with 32-bit byte offsets
+};
+
+struct XsumLayer {
+  const float* part;  // [splits][r][B*T]
+  void* Xt;           // [B][r][ldt]
+  int32_t splits;
+  int32_t block0;
+};
+struct XsumArgs {
+  XsumLayer L[kMaxLayers];
+  int32_t n_layers;
   int32_t B, T, r, ldt;
 };
 
@@ -76,11 +99,15 @@ struct SampArgs {
   int32_t n_layers;
   int32_t n_blocks;
   int32_t B, T, r, ldt;
-  int32_t groups;       // sum mode: sample groups
-  int32_t per_group;    // sum mode: samples per group
+  int32_t per_block;    // samples per block (norm: a run, sum: a group)
   int32_t n_slots;      // norm mode: partial slots per sample
-  float* norm_part;     // norm mode: [B][n_slots]
-  const float* scales;  // sum mode: [B]
+  int32_t off32;        // one sample's dY addressable with 32-bit byte offsets
+  float* norm_part;     // norm mode: [B][n_slots] (sum mode reads it when fused)
+  const float* scales;  // sum mode: [B] (unused when fused)
+  int32_t fuse_scale;   // sum mode: compute s_i from norm_part in the prologue
+  float clip_C;         // sum mode, fused
+  float* norms_out;     // sum mode, fused: [B] or null (written by layer 0's
+                        // first tile of each group)
 };
 
 // ---- n_i, s_i from the partials
@@ -110,28 +137,31 @@ struct FinArgs {
   uint32_t k0, k1, step_word;
 };
 
-// ---- Adam in the projected space; writes U transposed, Ut[n][j]
+// ---- update call, first launch: Adam on [r][d_out] (U written row-major in
+//      the operand type) and P regenerated row-major [r][d_in]
 struct AdamLayer {
   const float* g;
   float* m;
   float* v;
-  void* Ut;           // [d_out][ldr]
-  int32_t d_out;
+  void* U;            // [r][d_out]
   int32_t n_elem;     // r * d_out
   int32_t block0;
-  int32_t pad;
 };
-struct AdamArgs {
-  AdamLayer L[kMaxLayers];
+struct PrepArgs {
+  AdamLayer A[kMaxLayers];
+  GenPLayer P[kMaxLayers];
   int32_t n_layers;
-  int32_t r, ldr;
+  int32_t adam_blocks;  // blocks [0, adam_blocks) run Adam, the rest gen P
+  int32_t r;
   float beta1, beta2, one_m_beta1, one_m_beta2, bc1, bc2, eps;
+  float p_scale;
+  uint32_t k0, k1, step_word;
 };
 
-// ---- W -= lr Pt Ut^T
+// ---- W -= lr P^T U, reading P [r][d_in] and U [r][d_out] directly
 struct BackLayer {
-  const void* Pt;     // [d_in][ldr]
-  const void* Ut;     // [d_out][ldr]
+  const void* P;      // [r][d_in]
+  const void* U;      // [r][d_out]
   float* W;           // [d_in][d_out]
   int32_t d_in, d_out;
   int32_t m_tiles, n_tiles;
@@ -142,23 +172,26 @@ struct BackArgs {
   BackLayer L[kMaxLayers];
   int32_t n_layers;
   int32_t n_blocks;
-  int32_t r, ldr;
+  int32_t r;
   float lr;
+  int32_t off32;      // P and U addressable with 32-bit byte offsets
 };
 
 // Launchers (dpg_kernels.hip). Each returns the hipError_t of its launch.
 hipError_t launch_gen_p(const GenPArgs& a, int n_blocks, bool bf16_out,
-                        bool transposed, hipStream_t s);
+                        hipStream_t s);
 hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s);
+hipError_t launch_xsum(const XsumArgs& a, int n_blocks, bool bf16_out,
+                       hipStream_t s);
 hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
                             hipStream_t s);
 hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
                            hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, int B, hipStream_t s);
 hipError_t launch_fin(const FinArgs& a, int n_blocks, hipStream_t s);
-hipError_t launch_adam(const AdamArgs& a, int n_blocks, bool bf16_out,
+hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
                        hipStream_t s);
-hipError_t launch_back(const BackArgs& a, bool bf16_in, hipStream_t s);
+hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s);
 hipError_t launch_philox_normals(uint32_t k0, uint32_t k1, uint32_t layer_id,
                                  uint32_t step_word, uint32_t tag,
                                  uint32_t start, uint32_t n, float* z_out,

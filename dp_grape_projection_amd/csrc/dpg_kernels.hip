@@ -8,19 +8,27 @@
 //
 // Per-sample projected gradients are never stored. The projection call runs
 //   gen_p   P_l[r][d_in] from the seed (transient, bf16 or fp32)
-//   proj    Xt_l[b][j][t] = sum_k P_l[j][k] A_l[b][t][k]   (one GEMM over B*T)
+//   proj    Xt_l[b][j][t] = sum_k P_l[j][k] A_l[b][t][k] (one GEMM over all
+//           B*T rows, split over d_in when that balances the chip)
+//   xsum    sums the split partials of Xt (only for split layers)
 //   norm    for every (sample, tile): ||Xt_il dY_il||_F^2 partials
 //   scale   n_i = sqrt(sum of partials over all layers), s_i = min(1, C/n_i)
 //   sum     sum_i s_i Xt_il dY_il over groups of samples (second pass)
 //   fin     G_priv = (sum over groups + sigma C Z) / B
 // and the update call runs
-//   adam    m, v in place; U = mhat / (sqrt(vhat) + eps), written as Ut[n][j]
-//   gen_p   P_l again, transposed to Pt[k][j]
-//   back    W -= lr Pt Ut^T
+//   prep    Adam on [r][d_out] (m, v in place; U row-major) and P regenerated
+//   back    W -= lr P^T U
 #include "dpg_device.hpp"
 #include "dpg_internal.hpp"
 
 namespace dpg {
+
+template <typename T> struct StepK { static constexpr int v = sizeof(T) == 2 ? kStepBf16 : kStepF32; };
+template <typename T> using MainTile = Tile<T, kTileM, kTileN, StepK<T>::v, 4, 1>;
+
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
 
 template <class L>
 __device__ __forceinline__ int find_layer(const L* layers, int n, int b) {
@@ -28,6 +36,13 @@ __device__ __forceinline__ int find_layer(const L* layers, int n, int b) {
   for (int i = 1; i < n; ++i)
     if (b >= layers[i].block0) l = i;
   return l;
+}
+
+// Sum over the 64 lanes of a wave (butterfly, deterministic).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
 }
 
 // Sum over the 256 threads of a block, in a fixed order (deterministic).
@@ -42,31 +57,42 @@ __device__ __forceinline__ float block_sum(float x, float* red4) {
   return t;  // valid in thread 0 only
 }
 
+// Four values of T at dst (dst 4-element aligned).
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
+  typename Vec4<T>::type v;
+  v[0] = from_float<T>(a);
+  v[1] = from_float<T>(b);
+  v[2] = from_float<T>(c);
+  v[3] = from_float<T>(d);
+  *reinterpret_cast<typename Vec4<T>::type*>(dst) = v;
+}
+
 // ------------------------------------------------------------------ gen_p --
 
-template <typename T, bool TRANSPOSED>
-__global__ __launch_bounds__(kThreads) void gen_p_kernel(const GenPArgs a) {
-  const int b = blockIdx.x;
-  const GenPLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
-  const int c = (b - L.block0) * kThreads + static_cast<int>(threadIdx.x);
+// One thread per Philox counter c of one layer: elements e = 4c .. 4c+3 of
+// P (row-major, row stride ld).
+template <typename T>
+__device__ __forceinline__ void gen_p_thread(const GenPLayer& L, int c, int r,
+                                             float scale, const StreamKey& key) {
   if (c >= L.n_ctr) return;
-  const StreamKey key{a.k0, a.k1, a.step_word, 0u};
   float z[4];
   normals_at(key, L.layer_id, static_cast<uint32_t>(c), z);
-  const uint64_t total = static_cast<uint64_t>(a.r) * L.d_in;
-  uint64_t e = 4ull * static_cast<uint64_t>(c);
+  const uint64_t total = static_cast<uint64_t>(r) * L.d_in;
+  const uint64_t e = 4ull * static_cast<uint64_t>(c);
   uint32_t j = static_cast<uint32_t>(e / L.d_in);
   uint32_t k = static_cast<uint32_t>(e - static_cast<uint64_t>(j) * L.d_in);
   T* out = static_cast<T*>(L.out);
+  if ((L.d_in & 3) == 0 && (L.ld & 3) == 0) {
+    // the four elements lie in one row, 4-aligned
+    store4<T>(out + static_cast<int64_t>(j) * L.ld + k, z[0] * scale,
+              z[1] * scale, z[2] * scale, z[3] * scale);
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (e + q < total) {
-      const T val = from_float<T>(z[q] * a.scale);
-      if (TRANSPOSED)
-        out[static_cast<int64_t>(k) * L.ld + j] = val;
-      else
-        out[static_cast<int64_t>(j) * L.ld + k] = val;
-    }
+    if (e + q < total)
+      out[static_cast<int64_t>(j) * L.ld + k] = from_float<T>(z[q] * scale);
     if (++k == static_cast<uint32_t>(L.d_in)) {
       k = 0;
       ++j;
@@ -74,127 +100,234 @@ __global__ __launch_bounds__(kThreads) void gen_p_kernel(const GenPArgs a) {
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gen_p_kernel(const GenPArgs a) {
+  const int b = blockIdx.x;
+  const GenPLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
+  const StreamKey key{a.k0, a.k1, a.step_word, 0u};
+  gen_p_thread<T>(L, (b - L.block0) * kThreads + static_cast<int>(threadIdx.x),
+                  a.r, a.scale, key);
+}
+
 // ------------------------------------------------------------------- proj --
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void proj_kernel(const ProjArgs a) {
-  constexpr int BM = kProjBM, BN = kProjBN, BK = kProjBK;
-  typedef TileShape<T, BM, BN, BK> Sh;
-  __shared__ __attribute__((aligned(16))) T smem[(BM + BN) * Sh::S];
+__global__ __launch_bounds__(kThreads, 2) void proj_kernel(const ProjArgs a) {
+  typedef MainTile<T> Tl;
+  __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
-  const int tile = lb - L.block0;
-  const int mt = tile % L.m_tiles, nt = tile / L.m_tiles;
-  const int j0 = mt * BM, n0 = nt * BN;
+  const int local = lb - L.block0;
+  const int mt = local % L.m_tiles;
+  const int rest = local / L.m_tiles;
+  const int nt = rest % L.n_tiles;
+  const int split = rest / L.n_tiles;
+  const int j0 = mt * Tl::BM, n0 = nt * Tl::BN;
   const int BT = a.B * a.T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int n_steps_all = (L.d_in + Tl::BK - 1) / Tl::BK;
+  const int s_begin = split * L.steps_per_split;
+  const int s_end = min(n_steps_all, s_begin + L.steps_per_split);
 
-  RowsLoader<T, BM, BK, true> la{static_cast<const T*>(L.P) +
-                                     static_cast<int64_t>(j0) * L.ldp,
-                                 L.ldp, a.r - j0, L.d_in};
-  RowsLoader<T, BN, BK, VEC> lx{static_cast<const T*>(L.A) +
-                                    static_cast<int64_t>(n0) * L.d_in,
-                                L.d_in, BT - n0, L.d_in};
-  Acc<Sh::MB, Sh::NB> acc;
+  RowsLoader<T, Tl::BM, Tl::BK, true, IdentityRows> la{L.ldp, a.r - j0, L.d_in, {}};
+  RowsLoader<T, Tl::BN, Tl::BK, VEC, BOperandRows<Tl>> lx{L.d_in, BT - n0, L.d_in, {}};
+  const T* Pb = static_cast<const T*>(L.P) + static_cast<int64_t>(j0) * L.ldp;
+  const T* Ab = static_cast<const T*>(L.A) + static_cast<int64_t>(n0) * L.d_in;
+  Acc<Tl::MB, Tl::NB> acc;
   acc.zero();
-  k_loop<T, BM, BN, BK>(la, lx, smem, smem + BM * Sh::S, acc, 0, L.d_in, tid);
+  run_steps<T, Tl>(
+      la, lx, smem, acc, s_end - s_begin, tid,
+      [&](int s) {
+        const int k0 = (s_begin + s) * Tl::BK;
+        la.load(Pb, k0, tid, a.off32);
+        lx.load(Ab, k0, tid, a.off32);
+      },
+      [](int) {});
 
-  T* Xt = static_cast<T*>(L.Xt);
-#pragma unroll
-  for (int nb = 0; nb < Sh::NB; ++nb) {
-    const int n = n0 + acc_col<Sh::WTN>(wn, nb, lane);
-    if (n >= BT) continue;
-    const int bi = n / a.T, t = n - bi * a.T;
-    T* dst = Xt + static_cast<int64_t>(bi) * a.r * a.ldt + t;
-#pragma unroll
-    for (int mb = 0; mb < Sh::MB; ++mb)
+  // Each lane owns 4 consecutive columns n (= rows of A) of 16 rows j.
+  const int wm = Tl::wave_m(wave);
+  const int nq = n0 + Tl::acc_col(0, 0, lane);  // first of the 4 columns
+  if (L.splits == 1) {
+    T* Xt = static_cast<T*>(L.Xt);
+    if ((a.T & 3) == 0) {
+      if (nq >= BT) return;
+      const int bi = nq / a.T, t = nq - bi * a.T;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int j = j0 + acc_row<Sh::WTM>(wm, mb, i, lane);
+        const int j = j0 + Tl::acc_row(wm, 0, i, lane);
         if (j < a.r)
-          dst[static_cast<int64_t>(j) * a.ldt] = from_float<T>(acc.v[mb][nb][i]);
+          store4<T>(Xt + (static_cast<int64_t>(bi) * a.r + j) * a.ldt + t,
+                    acc.v[0][0][i], acc.v[0][1][i], acc.v[0][2][i], acc.v[0][3][i]);
       }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = nq + nb;
+        if (n >= BT) continue;
+        const int bi = n / a.T, t = n - bi * a.T;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = j0 + Tl::acc_row(wm, 0, i, lane);
+          if (j < a.r)
+            Xt[(static_cast<int64_t>(bi) * a.r + j) * a.ldt + t] =
+                from_float<T>(acc.v[0][nb][i]);
+        }
+      }
+    }
+  } else {
+    float* part = L.part + static_cast<int64_t>(split) * a.r * BT;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = j0 + Tl::acc_row(wm, 0, i, lane);
+      if (j >= a.r) continue;
+      float* dst = part + static_cast<int64_t>(j) * BT + nq;
+      if ((BT & 3) == 0) {
+        if (nq < BT)
+          *reinterpret_cast<f32x4*>(dst) = f32x4{acc.v[0][0][i], acc.v[0][1][i],
+                                                 acc.v[0][2][i], acc.v[0][3][i]};
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          if (nq + nb < BT) dst[nb] = acc.v[0][nb][i];
+      }
+    }
+  }
+}
+
+// Xt[b][j][t] = sum over splits of part[s][j][b*T + t]; one thread per 4
+// consecutive n of one row j.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
+  const int b = blockIdx.x;
+  const XsumLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
+  const int BT = a.B * a.T;
+  const int per_row = (BT + 3) / 4;
+  const int64_t idx = static_cast<int64_t>(b - L.block0) * kThreads + threadIdx.x;
+  if (idx >= static_cast<int64_t>(per_row) * a.r) return;
+  const int j = static_cast<int>(idx / per_row);
+  const int n = static_cast<int>(idx - static_cast<int64_t>(j) * per_row) * 4;
+  const int64_t plane = static_cast<int64_t>(a.r) * BT;
+  const float* src = L.part + static_cast<int64_t>(j) * BT + n;
+  T* Xt = static_cast<T*>(L.Xt);
+  if ((a.T & 3) == 0) {
+    f32x4 s = *reinterpret_cast<const f32x4*>(src);
+    for (int sp = 1; sp < L.splits; ++sp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + sp * plane);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+    const int bi = n / a.T, t = n - bi * a.T;
+    store4<T>(Xt + (static_cast<int64_t>(bi) * a.r + j) * a.ldt + t, s[0], s[1],
+              s[2], s[3]);
+  } else {
+    for (int q = 0; q < 4; ++q) {
+      if (n + q >= BT) break;
+      float s = src[q];
+      for (int sp = 1; sp < L.splits; ++sp) s += src[q + sp * plane];
+      const int bi = (n + q) / a.T, t = (n + q) - bi * a.T;
+      Xt[(static_cast<int64_t>(bi) * a.r + j) * a.ldt + t] = from_float<T>(s);
+    }
   }
 }
 
 // ---------------------------------------------------------- norm and sum --
 
+template <typename T, bool SUM> struct SampTileOf { typedef MainTile<T> type; };
+template <typename T> struct SampTileOf<T, true> {
+  typedef Tile<T, kTileM, kSumN, StepK<T>::v, 4, 1> type;
+};
+
+// n = sqrt(sum of one sample's norm partials), in slot order.
+__device__ __forceinline__ float sample_norm_seq(const float* part, int n_slots) {
+  float s = 0.0f;
+  for (int k = 0; k < n_slots; ++k) s += part[k];
+  return sqrtf(s);
+}
+
 template <typename T, bool PAIR, bool SUM>
-__global__ __launch_bounds__(kThreads) void samp_kernel(const SampArgs a) {
-  constexpr int BM = kSampBM, BN = kSampBN, BK = kSampBK;
-  typedef TileShape<T, BM, BN, BK> Sh;
-  __shared__ __attribute__((aligned(16))) T smem[(BM + BN) * Sh::S];
+__global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
+  typedef typename SampTileOf<T, SUM>::type Tl;
+  __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
   __shared__ float red4[4];
+  __shared__ float s_grp[SUM ? kFuseMaxGroup : 1];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const SampLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
-  const int tile = lb - L.block0;
-  const int mt = tile % L.m_tiles;
-  const int rest = tile / L.m_tiles;
+  const int li = find_layer(a.L, a.n_layers, lb);
+  const SampLayer& L = a.L[li];
+  const int local = lb - L.block0;
+  const int mt = local % L.m_tiles;
+  const int rest = local / L.m_tiles;
   const int nt = rest % L.n_tiles;
-  const int g = rest / L.n_tiles;  // sample (norm) or sample group (sum)
-  const int j0 = mt * BM, n0 = nt * BN;
+  const int g = rest / L.n_tiles;  // run (norm) or group (sum) of samples
+  const int j0 = mt * Tl::BM, n0 = nt * Tl::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int i_begin = g * a.per_block;
+  const int i_end = min(a.B, i_begin + a.per_block);
+  const int kc = (a.T + Tl::BK - 1) / Tl::BK;  // steps per sample
 
-  int i_begin = g, i_end = g + 1;
-  if (SUM) {
-    i_begin = g * a.per_group;
-    i_end = min(a.B, i_begin + a.per_group);
+  if (SUM && a.fuse_scale) {
+    // per-sample global norm and clip factor of this group (every block of
+    // the group computes the same values in the same order)
+    const int i = i_begin + tid;
+    if (i < i_end) {
+      const float n = sample_norm_seq(a.norm_part + static_cast<int64_t>(i) * a.n_slots,
+                                      a.n_slots);
+      s_grp[tid] = (n > a.clip_C) ? a.clip_C / n : 1.0f;
+      if (a.norms_out && li == 0 && mt == 0 && nt == 0) a.norms_out[i] = n;
+    }
+    // run_steps starts with a barrier, which publishes s_grp
   }
 
-  Acc<Sh::MB, Sh::NB> acc, tot;
-  if (SUM) tot.zero();
+  RowsLoader<T, Tl::BM, Tl::BK, true, IdentityRows> la{a.ldt, a.r - j0, a.T, {}};
+  ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lc{L.d_out, L.d_out - n0, a.T, {}};
   const T* Xt = static_cast<const T*>(L.Xt);
   const T* dY = static_cast<const T*>(L.dY);
-  for (int i = i_begin; i < i_end; ++i) {
-    RowsLoader<T, BM, BK, true> la{
-        Xt + (static_cast<int64_t>(i) * a.r + j0) * a.ldt, a.ldt, a.r - j0, a.T};
-    ColsLoader<T, BN, BK, PAIR> lc{
-        dY + static_cast<int64_t>(i) * a.T * L.d_out + n0, L.d_out,
-        L.d_out - n0, a.T};
-    acc.zero();
-    k_loop<T, BM, BN, BK>(la, lc, smem, smem + BM * Sh::S, acc, 0, a.T, tid);
-    if (SUM) {
-      const float s = a.scales[i];
-#pragma unroll
-      for (int mb = 0; mb < Sh::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < Sh::NB; ++nb)
-#pragma unroll
-          for (int q = 0; q < 16; ++q)
-            tot.v[mb][nb][q] = fmaf(s, acc.v[mb][nb][q], tot.v[mb][nb][q]);
-    } else {
-      // Out-of-range rows and columns were loaded as zeros, so they add 0.
-      float sq = 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < Sh::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < Sh::NB; ++nb)
-#pragma unroll
-          for (int q = 0; q < 16; ++q)
-            sq = fmaf(acc.v[mb][nb][q], acc.v[mb][nb][q], sq);
-      const float t = block_sum(sq, red4);
-      if (tid == 0)
-        a.norm_part[static_cast<int64_t>(i) * a.n_slots + L.slot0 +
-                    nt * L.m_tiles + mt] = t;
-    }
-  }
+
+  Acc<Tl::MB, Tl::NB> acc, tot;
+  acc.zero();
+  if (SUM) tot.zero();
+  run_steps<T, Tl>(
+      la, lc, smem, acc, (i_end - i_begin) * kc, tid,
+      [&](int s) {
+        const int i = i_begin + s / kc, k0 = (s % kc) * Tl::BK;
+        la.load(Xt + (static_cast<int64_t>(i) * a.r + j0) * a.ldt, k0, tid, a.off32);
+        lc.load(dY + static_cast<int64_t>(i) * a.T * L.d_out + n0, k0, tid, a.off32);
+      },
+      [&](int s) {
+        if (s % kc != kc - 1) return;
+        const int i = i_begin + s / kc;
+        if (SUM) {
+          tot.fma_from(a.fuse_scale ? s_grp[i - i_begin] : a.scales[i], acc);
+        } else {
+          // Rows and columns outside the layer were loaded as zeros.
+          const float t = wave_sum(acc.sum_sq());
+          if (lane == 0)
+            a.norm_part[static_cast<int64_t>(i) * a.n_slots +
+                        4 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+        }
+        acc.zero();
+      });
+
   if (SUM) {
+    static_assert(!SUM || Tl::NB == 2, "sum tile");
+    typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+    const int wm = Tl::wave_m(wave);
+    const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 2 columns
     float* part = L.part + static_cast<int64_t>(g) * a.r * L.d_out;
 #pragma unroll
-    for (int nb = 0; nb < Sh::NB; ++nb) {
-      const int n = n0 + acc_col<Sh::WTN>(wn, nb, lane);
-      if (n >= L.d_out) continue;
-#pragma unroll
-      for (int mb = 0; mb < Sh::MB; ++mb)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int j = j0 + acc_row<Sh::WTM>(wm, mb, q, lane);
-          if (j < a.r) part[static_cast<int64_t>(j) * L.d_out + n] = tot.v[mb][nb][q];
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int j = j0 + Tl::acc_row(wm, 0, i, lane);
+      if (j >= a.r || nq >= L.d_out) continue;
+      float* dst = part + static_cast<int64_t>(j) * L.d_out + nq;
+      if ((L.d_out & 1) == 0) {
+        *reinterpret_cast<f32x2*>(dst) = f32x2{tot.v[0][0][i], tot.v[0][1][i]};
+      } else {
+        dst[0] = tot.v[0][0][i];
+        if (nq + 1 < L.d_out) dst[1] = tot.v[0][1][i];
+      }
     }
   }
 }
@@ -228,6 +361,22 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
     const StreamKey key{a.k0, a.k1, a.step_word, 1u};
     normals_at(key, L.layer_id, static_cast<uint32_t>(c), z);
   }
+  if ((L.n_elem & 3) == 0) {
+    f32x4 s = *reinterpret_cast<const f32x4*>(L.part + e0);
+    for (int g = 1; g < a.groups; ++g) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(
+          L.part + g * static_cast<int64_t>(L.n_elem) + e0);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+    f32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = fmaf(a.noise_scale, z[q], s[q]) * a.inv_B;
+    *reinterpret_cast<f32x4*>(L.out + e0) = o;
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t e = e0 + q;
@@ -239,72 +388,150 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
   }
 }
 
-// ------------------------------------------------------------------- adam --
+// ------------------------------------------------------------------- prep --
+
+__device__ __forceinline__ float adam_dir(const PrepArgs& a, float g, float& m,
+                                          float& v) {
+  m = fmaf(a.beta1, m, a.one_m_beta1 * g);
+  v = fmaf(a.beta2, v, a.one_m_beta2 * (g * g));
+  return (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
+}
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void adam_kernel(const AdamArgs a) {
+__global__ __launch_bounds__(kThreads) void prep_kernel(const PrepArgs a) {
   const int b = blockIdx.x;
-  const AdamLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
+  if (b >= a.adam_blocks) {
+    const int bp = b - a.adam_blocks;
+    const GenPLayer& L = a.P[find_layer(a.P, a.n_layers, bp)];
+    const StreamKey key{a.k0, a.k1, a.step_word, 0u};
+    gen_p_thread<T>(L, (bp - L.block0) * kThreads + static_cast<int>(threadIdx.x),
+                    a.r, a.p_scale, key);
+    return;
+  }
+  const AdamLayer& L = a.A[find_layer(a.A, a.n_layers, b)];
   const int c = (b - L.block0) * kThreads + static_cast<int>(threadIdx.x);
   const int64_t e0 = 4ll * c;
   if (e0 >= L.n_elem) return;
-  T* Ut = static_cast<T*>(L.Ut);
+  T* U = static_cast<T*>(L.U);
+  if ((L.n_elem & 3) == 0) {
+    const f32x4 g = *reinterpret_cast<const f32x4*>(L.g + e0);
+    f32x4 m = *reinterpret_cast<const f32x4*>(L.m + e0);
+    f32x4 v = *reinterpret_cast<const f32x4*>(L.v + e0);
+    float u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float mq = m[q], vq = v[q];
+      u[q] = adam_dir(a, g[q], mq, vq);
+      m[q] = mq;
+      v[q] = vq;
+    }
+    *reinterpret_cast<f32x4*>(L.m + e0) = m;
+    *reinterpret_cast<f32x4*>(L.v + e0) = v;
+    store4<T>(U + e0, u[0], u[1], u[2], u[3]);
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t e = e0 + q;
     if (e < L.n_elem) {
-      const float g = L.g[e];
-      const float m = fmaf(a.beta1, L.m[e], a.one_m_beta1 * g);
-      const float v = fmaf(a.beta2, L.v[e], a.one_m_beta2 * (g * g));
+      float m = L.m[e], v = L.v[e];
+      const float u = adam_dir(a, L.g[e], m, v);
       L.m[e] = m;
       L.v[e] = v;
-      const float u = (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
-      const int64_t j = e / L.d_out, n = e - j * L.d_out;
-      Ut[n * a.ldr + j] = from_float<T>(u);
+      U[e] = from_float<T>(u);
     }
   }
 }
 
 // ------------------------------------------------------------------- back --
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void back_kernel(const BackArgs a) {
-  constexpr int BM = kBackBM, BN = kBackBN, BK = kBackBK;
-  typedef TileShape<T, BM, BN, BK> Sh;
-  __shared__ __attribute__((aligned(16))) T smem[(BM + BN) * Sh::S];
+template <typename T> using BackTile = Tile<T, kTileM, kBackN, StepK<T>::v, 4, 1>;
+
+template <typename T, bool PAIR>
+__global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
+  typedef BackTile<T> Tl;
+  static_assert(Tl::MB == 1 && Tl::NB == 2, "back tile");
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+  __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const BackLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
-  const int tile = lb - L.block0;
-  const int nt = tile % L.n_tiles, mt = tile / L.n_tiles;
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int local = lb - L.block0;
+  const int nt = local % L.n_tiles, mt = local / L.n_tiles;
+  const int m0 = mt * Tl::BM, n0 = nt * Tl::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = Tl::wave_m(wave);
+  const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 2 columns
+  const bool vec = (L.d_out & 1) == 0;
 
-  RowsLoader<T, BM, BK, true> la{static_cast<const T*>(L.Pt) +
-                                     static_cast<int64_t>(m0) * a.ldr,
-                                 a.ldr, L.d_in - m0, a.r};
-  RowsLoader<T, BN, BK, true> lu{static_cast<const T*>(L.Ut) +
-                                     static_cast<int64_t>(n0) * a.ldr,
-                                 a.ldr, L.d_out - n0, a.r};
-  Acc<Sh::MB, Sh::NB> acc;
-  acc.zero();
-  k_loop<T, BM, BN, BK>(la, lu, smem, smem + BM * Sh::S, acc, 0, a.r, tid);
-
+  // W rows of this lane (2 consecutive columns each), fetched before the
+  // operands so that both are in flight together.
+  // interior tile: every row and column in range (block-uniform)
+  const bool full = vec && m0 + Tl::BM <= L.d_in && n0 + Tl::BN <= L.d_out;
+  f32x2 w[16];
+  if (full) {
 #pragma unroll
-  for (int nb = 0; nb < Sh::NB; ++nb) {
-    const int n = n0 + acc_col<Sh::WTN>(wn, nb, lane);
-    if (n >= L.d_out) continue;
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + Tl::acc_row(wm, 0, i, lane);
+      w[i] = *reinterpret_cast<const f32x2*>(L.W + static_cast<int64_t>(m) * L.d_out + nq);
+    }
+  } else {
 #pragma unroll
-    for (int mb = 0; mb < Sh::MB; ++mb)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + acc_row<Sh::WTM>(wm, mb, q, lane);
-        if (m < L.d_in) {
-          float* w = L.W + static_cast<int64_t>(m) * L.d_out + n;
-          *w = fmaf(-a.lr, acc.v[mb][nb][q], *w);
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + Tl::acc_row(wm, 0, i, lane);
+      f32x2 x = {0.0f, 0.0f};
+      if (m < L.d_in && nq < L.d_out) {
+        const float* src = L.W + static_cast<int64_t>(m) * L.d_out + nq;
+        if (vec) {
+          x = *reinterpret_cast<const f32x2*>(src);
+        } else {
+          x[0] = src[0];
+          if (nq + 1 < L.d_out) x[1] = src[1];
         }
       }
+      w[i] = x;
+    }
+  }
+
+  ColsLoader<T, Tl::BM, Tl::BK, PAIR, IdentityRows> lp{L.d_in, L.d_in - m0, a.r, {}};
+  ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lu{L.d_out, L.d_out - n0, a.r, {}};
+  const T* Pb = static_cast<const T*>(L.P) + m0;
+  const T* Ub = static_cast<const T*>(L.U) + n0;
+  Acc<Tl::MB, Tl::NB> acc;
+  acc.zero();
+  run_steps<T, Tl>(
+      lp, lu, smem, acc, (a.r + Tl::BK - 1) / Tl::BK, tid,
+      [&](int s) {
+        lp.load(Pb, s * Tl::BK, tid, a.off32);
+        lu.load(Ub, s * Tl::BK, tid, a.off32);
+      },
+      [](int) {});
+
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + Tl::acc_row(wm, 0, i, lane);
+      f32x2 x = w[i];
+      x[0] = fmaf(-a.lr, acc.v[0][0][i], x[0]);
+      x[1] = fmaf(-a.lr, acc.v[0][1][i], x[1]);
+      *reinterpret_cast<f32x2*>(L.W + static_cast<int64_t>(m) * L.d_out + nq) = x;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + Tl::acc_row(wm, 0, i, lane);
+    if (m >= L.d_in || nq >= L.d_out) continue;
+    f32x2 x = w[i];
+    x[0] = fmaf(-a.lr, acc.v[0][0][i], x[0]);
+    x[1] = fmaf(-a.lr, acc.v[0][1][i], x[1]);
+    float* dst = L.W + static_cast<int64_t>(m) * L.d_out + nq;
+    if (vec) {
+      *reinterpret_cast<f32x2*>(dst) = x;
+    } else {
+      dst[0] = x[0];
+      if (nq + 1 < L.d_out) dst[1] = x[1];
+    }
   }
 }
 
@@ -333,6 +560,7 @@ __global__ __launch_bounds__(kThreads) void philox_normals_kernel(
   }
 }
 
+
 // -------------------------------------------------------------- launchers --
 
 static inline unsigned grid8(int n_blocks) {
@@ -340,15 +568,10 @@ static inline unsigned grid8(int n_blocks) {
 }
 
 hipError_t launch_gen_p(const GenPArgs& a, int n_blocks, bool bf16_out,
-                        bool transposed, hipStream_t s) {
+                        hipStream_t s) {
   const dim3 g(n_blocks), b(kThreads);
-  if (bf16_out) {
-    if (transposed) hipLaunchKernelGGL((gen_p_kernel<bf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((gen_p_kernel<bf16, false>), g, b, 0, s, a);
-  } else {
-    if (transposed) hipLaunchKernelGGL((gen_p_kernel<float, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((gen_p_kernel<float, false>), g, b, 0, s, a);
-  }
+  if (bf16_out) hipLaunchKernelGGL(gen_p_kernel<bf16>, g, b, 0, s, a);
+  else hipLaunchKernelGGL(gen_p_kernel<float>, g, b, 0, s, a);
   return hipGetLastError();
 }
 
@@ -361,6 +584,13 @@ hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s)
     if (vec) hipLaunchKernelGGL((proj_kernel<float, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((proj_kernel<float, false>), g, b, 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_xsum(const XsumArgs& a, int n_blocks, bool bf16_out,
+                       hipStream_t s) {
+  if (bf16_out) hipLaunchKernelGGL(xsum_kernel<bf16>, dim3(n_blocks), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(xsum_kernel<float>, dim3(n_blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -397,19 +627,23 @@ hipError_t launch_fin(const FinArgs& a, int n_blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_adam(const AdamArgs& a, int n_blocks, bool bf16_out,
+hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
                        hipStream_t s) {
   if (bf16_out)
-    hipLaunchKernelGGL(adam_kernel<bf16>, dim3(n_blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(prep_kernel<bf16>, dim3(n_blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(adam_kernel<float>, dim3(n_blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(prep_kernel<float>, dim3(n_blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_back(const BackArgs& a, bool bf16_in, hipStream_t s) {
+hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
-  if (bf16_in) hipLaunchKernelGGL(back_kernel<bf16>, g, b, 0, s, a);
-  else hipLaunchKernelGGL(back_kernel<float>, g, b, 0, s, a);
+  if (bf16_in) {
+    if (pair) hipLaunchKernelGGL((back_kernel<bf16, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((back_kernel<bf16, false>), g, b, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((back_kernel<float, true>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 
