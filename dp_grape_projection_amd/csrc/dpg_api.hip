@@ -136,7 +136,7 @@ struct ProjPlan {
   std::vector<int64_t> ldp;    // row stride of P per layer
   std::vector<size_t> off_P, off_Xt, off_part, off_xpart;
   std::vector<int32_t> m_tiles, n_tiles_proj, splits, steps_per_split;
-  std::vector<int32_t> n_tiles_s, n_tiles_sum, slot0;
+  std::vector<int32_t> n_tiles_s, slot0;  // per-sample passes: tiles over d_out
   int32_t n_slots = 0;
   int32_t norm_per_block = 1;  // samples per norm block
   int32_t groups = 1, per_group = 1;  // sum pass
@@ -182,7 +182,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   const int64_t target = target_blocks(dtype);
   const int64_t steps_per_block = std::max<int64_t>(1, ceil_div(units, target));
   size_t off = 0;
-  int64_t tiles_s = 0, tiles_sum = 0;
+  int64_t tiles_s = 0;
   for (int l = 0; l < n_layers; ++l) {
     const int64_t ldp = round_up(layers[l].d_in, 8);
     p.ldp.push_back(ldp);
@@ -202,8 +202,6 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     if (splits > 1) off = align_up(off + static_cast<size_t>(splits) * r * BT * 4);
     const int32_t nt = static_cast<int32_t>(ceil_div(layers[l].d_out, kTileN));
     p.n_tiles_s.push_back(nt);
-    p.n_tiles_sum.push_back(static_cast<int32_t>(ceil_div(layers[l].d_out, kSumN)));
-    tiles_sum += static_cast<int64_t>(mt) * p.n_tiles_sum.back();
     p.slot0.push_back(p.n_slots / 4);
     p.n_slots += 4 * mt * nt;  // one partial per wave
     tiles_s += static_cast<int64_t>(mt) * nt;
@@ -228,7 +226,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     int64_t best = -1;
     for (int64_t per = B; per >= 1; --per) {
       const int64_t g = ceil_div(B, per);
-      const int64_t cost = ceil_div(tiles_sum * g, target) * per;
+      const int64_t cost = ceil_div(tiles_s * g, target) * per;
       if (best < 0 || cost < best) {
         best = cost;
         p.per_group = static_cast<int32_t>(per);
@@ -490,7 +488,7 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
       L.part = reinterpret_cast<float*>(ws + p.off_part[l]);
       L.d_out = static_cast<int32_t>(layers[l].d_out);
       L.m_tiles = p.m_tiles[l];
-      L.n_tiles = sum ? p.n_tiles_sum[l] : p.n_tiles_s[l];
+      L.n_tiles = p.n_tiles_s[l];
       L.slot0 = p.slot0[l];
       L.block0 = blocks;
       blocks += static_cast<int>(L.m_tiles * L.n_tiles * runs);

@@ -169,13 +169,13 @@ struct Acc {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[a][b][i] = 0.0f;
   }
-  __device__ __forceinline__ void fma_from(float s, const Acc& o) {
+  __device__ __forceinline__ void scale(float s) {
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[a][b][i] = fmaf(s, o.v[a][b][i], v[a][b][i]);
+        for (int i = 0; i < 16; ++i) v[a][b][i] *= s;
   }
   __device__ __forceinline__ float sum_sq() const {
     float s = 0.0f;
@@ -484,12 +484,17 @@ struct ColsLoader<float, COLS, BK, PAIR, Map> {
 
 // Runs n_steps BK-deep steps. load_step(s) issues the global loads of step s
 // into the loaders' registers; the loads of step s + 1 are in flight while
-// step s runs on the matrix cores. after_step(s) runs once step s has been
-// accumulated.
-template <typename T, class Tl, class LA, class LB, class LoadStep, class AfterStep>
+// step s runs on the matrix cores. prologue() runs once, after the loads of
+// step 0 are issued and before the first barrier (its LDS writes are visible
+// to pre_step). pre_step(s) runs before step s is accumulated and returns
+// whether to accumulate it (the same value in every thread of the block);
+// after_step(s) runs once step s has been accumulated.
+template <typename T, class Tl, class LA, class LB, class LoadStep, class Prologue,
+          class PreStep, class AfterStep>
 __device__ __forceinline__ void run_steps(LA& la, LB& lb, T* smem,
                                           Acc<Tl::MB, Tl::NB>& acc, int n_steps,
                                           int tid, LoadStep load_step,
+                                          Prologue prologue, PreStep pre_step,
                                           AfterStep after_step) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = Tl::wave_m(wave), wn = Tl::wave_n(wave);
@@ -497,15 +502,25 @@ __device__ __forceinline__ void run_steps(LA& la, LB& lb, T* smem,
   T* sB = smem + Tl::BM * Tl::S;
   if (n_steps <= 0) return;
   load_step(0);
+  prologue();
   for (int s = 0; s < n_steps; ++s) {
     __syncthreads();  // the previous step finished reading LDS
     la.store(sA, tid);
     lb.store(sB, tid);
     __syncthreads();
     if (s + 1 < n_steps) load_step(s + 1);
-    Mma<T, Tl>::run(sA, sB, acc, wm, wn, lane);
+    if (pre_step(s)) Mma<T, Tl>::run(sA, sB, acc, wm, wn, lane);
     after_step(s);
   }
+}
+
+template <typename T, class Tl, class LA, class LB, class LoadStep, class AfterStep>
+__device__ __forceinline__ void run_steps(LA& la, LB& lb, T* smem,
+                                          Acc<Tl::MB, Tl::NB>& acc, int n_steps,
+                                          int tid, LoadStep load_step,
+                                          AfterStep after_step) {
+  run_steps<T, Tl>(la, lb, smem, acc, n_steps, tid, load_step, [] {},
+                   [](int) { return true; }, after_step);
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).

@@ -16,7 +16,6 @@ constexpr int kMaxLayers = 32;
 // bf16 operands and 32 for fp32 operands.
 constexpr int kTileM = 128, kTileN = 128;
 constexpr int kBackN = 64;  // back-projection: 128 x 64 output tiles
-constexpr int kSumN = 64;   // clipped-sum pass: 128 x 64 output tiles
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this
 // many norm partials.

@@ -235,23 +235,17 @@ __global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
 
 // ---------------------------------------------------------- norm and sum --
 
-template <typename T, bool SUM> struct SampTileOf { typedef MainTile<T> type; };
-template <typename T> struct SampTileOf<T, true> {
-  typedef Tile<T, kTileM, kSumN, StepK<T>::v, 4, 1> type;
-};
-
-// n = sqrt(sum of one sample's norm partials), in slot order.
-__device__ __forceinline__ float sample_norm_seq(const float* part, int n_slots) {
-  float s = 0.0f;
-  for (int k = 0; k < n_slots; ++k) s += part[k];
-  return sqrtf(s);
-}
-
+// Norm mode: squared-norm partials of Xt_i dY_i per (sample, tile, wave).
+// Sum mode: sum_i s_i Xt_i dY_i over a group of samples, into one fp32
+// partial per (group, tile). The sum keeps a single accumulator R expressed
+// in units of the current sample's clip factor: before sample i it is
+// rescaled by c / s_i (c = the factor of the previous sample), the sample's
+// product is added by the matrix cores, and the final R is multiplied by the
+// last factor. A sample with s_i = 0 (its norm overflowed) is skipped.
 template <typename T, bool PAIR, bool SUM>
 __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
-  typedef typename SampTileOf<T, SUM>::type Tl;
+  typedef MainTile<T> Tl;
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
-  __shared__ float red4[4];
   __shared__ float s_grp[SUM ? kFuseMaxGroup : 1];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
@@ -268,27 +262,15 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
   const int i_end = min(a.B, i_begin + a.per_block);
   const int kc = (a.T + Tl::BK - 1) / Tl::BK;  // steps per sample
 
-  if (SUM && a.fuse_scale) {
-    // per-sample global norm and clip factor of this group (every block of
-    // the group computes the same values in the same order)
-    const int i = i_begin + tid;
-    if (i < i_end) {
-      const float n = sample_norm_seq(a.norm_part + static_cast<int64_t>(i) * a.n_slots,
-                                      a.n_slots);
-      s_grp[tid] = (n > a.clip_C) ? a.clip_C / n : 1.0f;
-      if (a.norms_out && li == 0 && mt == 0 && nt == 0) a.norms_out[i] = n;
-    }
-    // run_steps starts with a barrier, which publishes s_grp
-  }
-
   RowsLoader<T, Tl::BM, Tl::BK, true, IdentityRows> la{a.ldt, a.r - j0, a.T, {}};
   ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lc{L.d_out, L.d_out - n0, a.T, {}};
   const T* Xt = static_cast<const T*>(L.Xt);
   const T* dY = static_cast<const T*>(L.dY);
 
-  Acc<Tl::MB, Tl::NB> acc, tot;
+  Acc<Tl::MB, Tl::NB> acc;
   acc.zero();
-  if (SUM) tot.zero();
+  float c = 0.0f;  // sum mode: factor R is expressed in (0 while R is empty)
+  bool on = true;  // sum mode: the current sample is accumulated
   run_steps<T, Tl>(
       la, lc, smem, acc, (i_end - i_begin) * kc, tid,
       [&](int s) {
@@ -296,37 +278,73 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
         la.load(Xt + (static_cast<int64_t>(i) * a.r + j0) * a.ldt, k0, tid, a.off32);
         lc.load(dY + static_cast<int64_t>(i) * a.T * L.d_out + n0, k0, tid, a.off32);
       },
-      [&](int s) {
-        if (s % kc != kc - 1) return;
-        const int i = i_begin + s / kc;
-        if (SUM) {
-          tot.fma_from(a.fuse_scale ? s_grp[i - i_begin] : a.scales[i], acc);
-        } else {
-          // Rows and columns outside the layer were loaded as zeros.
-          const float t = wave_sum(acc.sum_sq());
-          if (lane == 0)
-            a.norm_part[static_cast<int64_t>(i) * a.n_slots +
-                        4 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+      [&] {
+        if (!SUM || !a.fuse_scale) return;
+        // Per-sample global norm and clip factor of this group: wave w takes
+        // samples w, w + 4, ...; lane l adds slots l, l + 64, ... in order,
+        // then the lanes are combined by a fixed butterfly. Every block of
+        // the group computes the same values.
+        const int jn = (a.n_slots + 63) >> 6;  // <= kFuseMaxSlots / 64
+        for (int q = wave; q < i_end - i_begin; q += 4) {
+          const float* p = a.norm_part + static_cast<int64_t>(i_begin + q) * a.n_slots;
+          float v[kFuseMaxSlots / 64];
+#pragma unroll
+          for (int j = 0; j < kFuseMaxSlots / 64; ++j)
+            if (j < jn) v[j] = p[min(lane + 64 * j, a.n_slots - 1)];
+          float t = 0.0f;
+#pragma unroll
+          for (int j = 0; j < kFuseMaxSlots / 64; ++j)
+            if (j < jn && lane + 64 * j < a.n_slots) t += v[j];
+          const float n = sqrtf(wave_sum(t));
+          if (lane == 0) {
+            s_grp[q] = (n > a.clip_C) ? a.clip_C / n : 1.0f;
+            if (a.norms_out && li == 0 && mt == 0 && nt == 0) a.norms_out[i_begin + q] = n;
+          }
         }
+      },
+      [&](int s) -> bool {
+        if (!SUM) return true;
+        if (s % kc == 0) {
+          const int i = i_begin + s / kc;
+          const float si = a.fuse_scale ? s_grp[i - i_begin] : a.scales[i];
+          on = si > 0.0f;
+          if (on) {
+            if (c != 0.0f && c != si) acc.scale(c / si);
+            c = si;
+          }
+        }
+        return on;
+      },
+      [&](int s) {
+        if (SUM || s % kc != kc - 1) return;
+        // Rows and columns outside the layer were loaded as zeros.
+        const int i = i_begin + s / kc;
+        const float t = wave_sum(acc.sum_sq());
+        if (lane == 0)
+          a.norm_part[static_cast<int64_t>(i) * a.n_slots +
+                      4 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
         acc.zero();
       });
 
   if (SUM) {
-    static_assert(!SUM || Tl::NB == 2, "sum tile");
-    typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+    static_assert(Tl::MB == 1 && Tl::NB == 4 && Tl::WGN == 1, "sum tile");
+    acc.scale(c);
     const int wm = Tl::wave_m(wave);
-    const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 2 columns
+    const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 4 columns
     float* part = L.part + static_cast<int64_t>(g) * a.r * L.d_out;
+    const bool vec = (L.d_out & 3) == 0 && nq + 3 < L.d_out;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = j0 + Tl::acc_row(wm, 0, i, lane);
       if (j >= a.r || nq >= L.d_out) continue;
       float* dst = part + static_cast<int64_t>(j) * L.d_out + nq;
-      if ((L.d_out & 1) == 0) {
-        *reinterpret_cast<f32x2*>(dst) = f32x2{tot.v[0][0][i], tot.v[0][1][i]};
+      if (vec) {
+        *reinterpret_cast<f32x4*>(dst) =
+            f32x4{acc.v[0][0][i], acc.v[0][1][i], acc.v[0][2][i], acc.v[0][3][i]};
       } else {
-        dst[0] = tot.v[0][0][i];
-        if (nq + 1 < L.d_out) dst[1] = tot.v[0][1][i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (nq + q < L.d_out) dst[q] = acc.v[0][q][i];
       }
     }
   }

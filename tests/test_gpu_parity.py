@@ -82,6 +82,19 @@ CASES = {
     "many_layers": W.custom_workload("many_layers", 17,
                                      [(24, 16), (16, 24)] * 20, B=2, T=8,
                                      r=8, layer_ids=list(range(100, 140))),
+    # more than 1024 norm partials per sample: clip factors come from the
+    # separate scale launch instead of the sum pass's prologue
+    "wide_unfused_bf16": W.custom_workload("wide_unfused_bf16", 18,
+                                           [(64, 17920), (48, 16640)], B=3,
+                                           T=8, r=16),
+    # enough tiles x samples that the sum pass adds several samples per
+    # block (groups of 7), each with its own clip factor
+    "groups_bf16": W.custom_workload("groups_bf16", 19,
+                                     [(32, 6400), (32, 6400)], B=33, T=8,
+                                     r=16),
+    "groups_fp32": W.custom_workload("groups_fp32", 20,
+                                     [(32, 6400), (32, 6400)], B=33, T=8,
+                                     r=16, dtype="fp32"),
 }
 
 
@@ -175,9 +188,10 @@ def test_no_clipping_is_plain_mean():
         assert rel_fro(g, w) <= TOL["bf16"]
 
 
-def test_mixed_clipping():
+@pytest.mark.parametrize("name", ["ragged_bf16", "groups_bf16", "groups_fp32"])
+def test_mixed_clipping(name):
     """C near the median norm: some samples clipped, some not."""
-    wl = CASES["ragged_bf16"]
+    wl = CASES[name]
     host, orc, _ = make_case(wl)
     n = oracle.project_clip_noise(orc, wl.r, math.inf, 0.0, wl.seed, wl.step,
                                   wl.proj_step)["norms"]
