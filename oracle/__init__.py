@@ -25,5 +25,6 @@ from .dpgrape import (  # noqa: F401
     TAG_PROJECTION, TAG_NOISE,
     projection_matrix, noise_matrix, per_sample_gradient,
     project_clip_noise, adam_update, backproject_delta, adam_backproject,
-    naive_privatise_then_project, sample_norms,
+    naive_privatise_then_project, sample_norms, clip_scale,
+    projection_rows, noise_rows, g_priv_rows,
 )

@@ -223,6 +223,49 @@ def adam_backproject(params: Sequence[dict], r: int, lr: float, beta1: float,
     return out
 
 
+def projection_rows(seed: int, layer_id: int, proj_step: int, r: int,
+                    d_in: int, rows: Sequence[int]) -> np.ndarray:
+    """Rows `rows` of P_l (same stream as projection_matrix: row j holds
+    elements j*d_in .. j*d_in + d_in - 1)."""
+    out = np.empty((len(rows), d_in), dtype=np.float64)
+    for a, j in enumerate(rows):
+        out[a] = gaussian_stream(seed, layer_id, proj_step, TAG_PROJECTION,
+                                 d_in, start=int(j) * d_in)
+    return out / math.sqrt(r)
+
+
+def noise_rows(seed: int, layer_id: int, step: int, r: int, d_out: int,
+               rows: Sequence[int]) -> np.ndarray:
+    """Rows `rows` of Z_l (same stream as noise_matrix)."""
+    out = np.empty((len(rows), d_out), dtype=np.float64)
+    for a, j in enumerate(rows):
+        out[a] = gaussian_stream(seed, layer_id, step, TAG_NOISE, d_out,
+                                 start=int(j) * d_out)
+    return out
+
+
+def g_priv_rows(A: np.ndarray, dY: np.ndarray, P_rows: np.ndarray,
+                scales: np.ndarray, clip_C: float, sigma: float,
+                Z_rows: Optional[np.ndarray]) -> np.ndarray:
+    """Rows of G_priv_l = (sum_i s_i P_l G_il + sigma C Z_l) / B for given
+    rows of P_l and Z_l and given clip factors s_i, for inputs too large to
+    project whole.
+
+    Row j of P_l G_il is p_j A_i^T dY_i; it is evaluated as (A_i p_j)^T dY_i,
+    the same product associated the other way (exact in real arithmetic,
+    pinned against project_clip_noise in the tests)."""
+    A = np.asarray(A, np.float64)
+    dY = np.asarray(dY, np.float64)
+    B = A.shape[0]
+    acc = np.zeros((P_rows.shape[0], dY.shape[2]), dtype=np.float64)
+    for i in range(B):
+        x = A[i] @ P_rows.T            # [T, rows]
+        acc += scales[i] * (x.T @ dY[i])
+    if sigma > 0:
+        acc += sigma * clip_C * Z_rows
+    return acc / B
+
+
 def naive_privatise_then_project(layers: Sequence[dict], r: int,
                                  clip_C: float, sigma: float, seed: int,
                                  step: int, proj_step: int) -> List[np.ndarray]:

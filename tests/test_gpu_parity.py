@@ -82,6 +82,12 @@ CASES = {
     "many_layers": W.custom_workload("many_layers", 17,
                                      [(24, 16), (16, 24)] * 20, B=2, T=8,
                                      r=8, layer_ids=list(range(100, 140))),
+    # bf16 projection on the LDS ring: full 128 x 64 tiles next to ragged
+    # ones (r = 160, B*T = 600) and a ragged contraction tail (d_in = 200,
+    # 328)
+    "ring_edges_bf16": W.custom_workload("ring_edges_bf16", 21,
+                                         [(200, 96), (328, 40)], B=2, T=300,
+                                         r=160),
     # more than 1024 norm partials per sample: clip factors come from the
     # separate scale launch instead of the sum pass's prologue
     "wide_unfused_bf16": W.custom_workload("wide_unfused_bf16", 18,

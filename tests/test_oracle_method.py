@@ -305,3 +305,37 @@ def test_identity_projection_reduces_to_dp_adam():
         for l in range(2):
             np.testing.assert_allclose(Ws[l], tW[l].detach().numpy(),
                                        rtol=1e-10, atol=1e-12)
+
+
+# --- row-wise helpers used by the full-size sampled checks ------------------
+
+def test_projection_and_noise_rows_match_full_matrices():
+    """projection_rows / noise_rows are rows of projection_matrix /
+    noise_matrix (same streams and element numbering)."""
+    r, d_in, d_out = 7, 13, 11
+    P = oracle.projection_matrix(5, 3, 2, r, d_in)
+    Z = oracle.noise_matrix(5, 3, 4, r, d_out)
+    rows = [0, 3, 6]
+    np.testing.assert_array_equal(oracle.projection_rows(5, 3, 2, r, d_in, rows), P[rows])
+    np.testing.assert_array_equal(oracle.noise_rows(5, 3, 4, r, d_out, rows), Z[rows])
+
+
+@pytest.mark.parametrize("sigma", [0.0, 0.7])
+def test_g_priv_rows_match_the_full_step(sigma):
+    """g_priv_rows (given the step's clip factors) reproduces rows of the full
+    oracle's G_priv, clipped samples and noise included."""
+    rng = np.random.default_rng(11)
+    B, T, r = 5, 6, 9
+    layers = _layers(rng, B, T, [(10, 8), (8, 12)], ids=[4, 7])
+    C = float(np.median(oracle.sample_norms(layers, r, 3, 2)))
+    full = oracle.project_clip_noise(layers, r, C, sigma, 3, 5, 2)
+    assert (full["scales"] < 1).any() and (full["scales"] == 1).any()
+    rows = [0, 4, 8]
+    for l, lay in enumerate(layers):
+        d_in, d_out = lay["A"].shape[2], lay["dY"].shape[2]
+        Pr = oracle.projection_rows(3, lay["layer_id"], 2, r, d_in, rows)
+        Zr = oracle.noise_rows(3, lay["layer_id"], 5, r, d_out, rows)
+        got = oracle.g_priv_rows(lay["A"], lay["dY"], Pr, full["scales"], C,
+                                 sigma, Zr)
+        np.testing.assert_allclose(got, full["G_priv"][l][rows], rtol=1e-12,
+                                   atol=1e-14)

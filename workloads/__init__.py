@@ -213,3 +213,66 @@ def as_float64(wl: Workload, x: np.ndarray) -> np.ndarray:
     if wl.dtype == "bf16":
         return f32_from_bf16_bits(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+# ------------------------------------------------ draws in device memory --
+#
+# The large workloads (enc12, dec24, long1: 2 to 15 GB of A and dY) are drawn
+# directly in device memory with torch's seeded generator, since drawing them
+# on the host takes minutes. The values differ from the host draws above (a
+# different generator) but follow the same distributions; checks read host
+# copies of the slices they need. Seeds: (index << 40) | (layer id << 8) |
+# tensor id.
+
+def _device_gen(wl: Workload, layer_id: int, tensor_id: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((wl.index << 40) | (int(layer_id) << 8) | tensor_id)
+    return g
+
+
+def device_layer_inputs(wl: Workload, layer: Layer, device="cuda"):
+    """(A, dY) for one layer as torch tensors on `device`, in the workload's
+    element type (fp32 draws, rounded to bf16 by torch's round-to-nearest-even
+    conversion for bf16 workloads)."""
+    import torch
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    f32 = torch.float32
+    gA = _device_gen(wl, layer.layer_id, 0, device)
+    A = torch.randn((wl.B, wl.T, layer.d_in), generator=gA, device=device, dtype=f32)
+    if wl.a_kind == "fan_in":
+        A.mul_(1.0 / np.sqrt(layer.d_in))
+    elif wl.a_kind != "unit":
+        raise ValueError(wl.a_kind)
+    gD = _device_gen(wl, layer.layer_id, 1, device)
+    shape = (wl.B, wl.T, layer.d_out)
+    if wl.dy_kind == "inv_T":
+        dY = torch.randn(shape, generator=gD, device=device, dtype=f32)
+        dY.mul_(1.0 / np.sqrt(wl.T))
+    elif wl.dy_kind == "inv_Tdout":
+        dY = torch.randn(shape, generator=gD, device=device, dtype=f32)
+        dY.mul_(1.0 / np.sqrt(wl.T * layer.d_out))
+    elif wl.dy_kind == "t3_inv_Tdout":
+        # Student-t with 3 degrees of freedom: z / sqrt(chi2_3 / 3)
+        dY = torch.randn(shape, generator=gD, device=device, dtype=f32)
+        chi2 = torch.zeros(shape, device=device, dtype=f32)
+        for _ in range(3):
+            c = torch.randn(shape, generator=gD, device=device, dtype=f32)
+            chi2.addcmul_(c, c)
+        dY.div_(torch.sqrt(chi2 / 3.0))
+        dY.mul_(1.0 / np.sqrt(wl.T * layer.d_out))
+    else:
+        raise ValueError(wl.dy_kind)
+    return A.to(dt), dY.to(dt)
+
+
+def device_initial_state(wl: Workload, layer: Layer, device="cuda"):
+    """(W, m, v) on `device`: W ~ N(0, 1/d_in) fp32, m = v = 0."""
+    import torch
+    g = _device_gen(wl, layer.layer_id, 2, device)
+    W = torch.randn((layer.d_in, layer.d_out), generator=g, device=device,
+                    dtype=torch.float32)
+    W.mul_(1.0 / np.sqrt(layer.d_in))
+    m = torch.zeros((wl.r, layer.d_out), device=device, dtype=torch.float32)
+    v = torch.zeros_like(m)
+    return W, m, v
