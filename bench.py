@@ -41,7 +41,45 @@ def parse():
                     help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after the steps, copy a buffer of this many MiB "
+                         "three times (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mlp4_hbm_traffic.md")
+
+
+def kernel_source_digest():
+    """sha256 over the library's kernel and launch sources (the counters in
+    the traffic summary hold only for the sources they were taken on)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dp_grape_projection_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) +
+                    glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None when
+    there is none for this workload or the kernels changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            text = fh.read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("workload") != workload or data.get("source_sha256") != kernel_source_digest():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def kernel_work(wl):
@@ -206,9 +244,19 @@ def main():
         dk = kernels[dom]
         roof = {"kernel": dom, "bound": "hbm", "achieved": dk["GB/s"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, wl.name),
                 "mfma_TFLOP/s": dk["TFLOP/s"],
                 "mfma_frac": round(dk["TFLOP/s"] / peak_flops, 4)}
+
+    if args.copy_mb > 0:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -139,6 +139,7 @@ struct ProjPlan {
   std::vector<int32_t> n_tiles_s, slot0;  // per-sample passes: tiles over d_out
   int32_t n_slots = 0;
   int32_t norm_per_block = 1;  // samples per norm block
+  int32_t norm_res_tiles = 0;  // column tiles per norm block (T within one step)
   int32_t groups = 1, per_group = 1;  // sum pass
   bool fuse_scale = false;             // sum pass computes s_i itself
   size_t off_norm = 0, off_scales = 0, total = 0;
@@ -174,13 +175,16 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   const int64_t BT = B * T;
   p.ldt = round_up(T, 8);
   const int32_t mt = static_cast<int32_t>(ceil_div(r, kTileM));
-  // Projection: K steps per block chosen so that about kTargetBlocks blocks
-  // share the work; a layer whose d_in needs more steps is split over d_in.
+  // Projection: K steps per block chosen so that about half of `target`
+  // blocks share the work; a layer whose d_in needs more steps is split over
+  // d_in. Every split writes an fp32 partial of Xt that the xsum kernel reads
+  // back, so splits are kept twice as long as one round of resident blocks
+  // would need.
   int64_t units = 0;
   for (int l = 0; l < n_layers; ++l)
     units += mt * ceil_div(BT, kTileN) * ceil_div(layers[l].d_in, BK);
   const int64_t target = target_blocks(dtype);
-  const int64_t steps_per_block = std::max<int64_t>(1, ceil_div(units, target));
+  const int64_t steps_per_block = std::max<int64_t>(1, ceil_div(units, target / 2));
   size_t off = 0;
   int64_t tiles_s = 0;
   for (int l = 0; l < n_layers; ++l) {
@@ -209,7 +213,24 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // Both per-sample passes give each block a run of samples of one tile. The
   // run length is chosen to minimise (rounds of resident blocks) x (samples
   // per block), so that the last round is not a small fraction of the chip.
-  // Norm pass: runs of up to 8 samples (ties: the longer run).
+  // Norm pass, T within one step: one sample per block, which keeps its Xt
+  // tile in LDS over a run of column tiles (ties: the longer run).
+  if (ceil_div(T, BK) == 1) {
+    int64_t best = -1, max_nt = 1;
+    for (int l = 0; l < n_layers; ++l)
+      max_nt = std::max<int64_t>(max_nt, ceil_div(layers[l].d_out, kTileN));
+    for (int64_t per = 1; per <= max_nt; ++per) {
+      int64_t blocks = 0;
+      for (int l = 0; l < n_layers; ++l)
+        blocks += mt * B * ceil_div(ceil_div(layers[l].d_out, kTileN), per);
+      const int64_t cost = ceil_div(blocks, target) * per;
+      if (best < 0 || cost <= best) {
+        best = cost;
+        p.norm_res_tiles = static_cast<int32_t>(per);
+      }
+    }
+  }
+  // Norm pass otherwise: runs of up to 8 samples (ties: the longer run).
   {
     int64_t best = -1;
     for (int64_t pb = 1; pb <= std::min<int64_t>(8, B); ++pb) {
@@ -472,6 +493,7 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     a.r = r;
     a.ldt = static_cast<int32_t>(p.ldt);
     a.per_block = sum ? p.per_group : p.norm_per_block;
+    a.res_tiles = sum ? 0 : p.norm_res_tiles;
     a.n_slots = p.n_slots;
     a.norm_part = norm_part;
     a.scales = scales;
@@ -491,7 +513,12 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
       L.n_tiles = p.n_tiles_s[l];
       L.slot0 = p.slot0[l];
       L.block0 = blocks;
-      blocks += static_cast<int>(L.m_tiles * L.n_tiles * runs);
+      if (a.res_tiles > 0) {
+        L.n_chunks = static_cast<int32_t>(ceil_div(L.n_tiles, a.res_tiles));
+        blocks += static_cast<int>(L.m_tiles * L.n_chunks * B);
+      } else {
+        blocks += static_cast<int>(L.m_tiles * L.n_tiles * runs);
+      }
       // bf16: dY is gathered two columns (4 bytes) at a time
       *pair = *pair && layers[l].d_out % 2 == 0 && aligned(layers[l].dY, 4);
     }

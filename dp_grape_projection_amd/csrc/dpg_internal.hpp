@@ -91,7 +91,7 @@ struct SampLayer {
   int32_t n_tiles;    // over d_out
   int32_t slot0;      // norm mode: first partial slot of this layer
   int32_t block0;
-  int32_t pad;
+  int32_t n_chunks;   // norm mode with res_tiles: runs of column tiles per sample
 };
 struct SampArgs {
   SampLayer L[kMaxLayers];
@@ -99,6 +99,9 @@ struct SampArgs {
   int32_t n_blocks;
   int32_t B, T, r, ldt;
   int32_t per_block;    // samples per block (norm: a run, sum: a group)
+  int32_t res_tiles;    // norm mode, T within one step: a block keeps one
+                        // sample's Xt tile in LDS and sweeps this many
+                        // column tiles of its dY (0: runs of samples)
   int32_t n_slots;      // norm mode: partial slots per sample
   int32_t off32;        // one sample's dY addressable with 32-bit byte offsets
   float* norm_part;     // norm mode: [B][n_slots] (sum mode reads it when fused)

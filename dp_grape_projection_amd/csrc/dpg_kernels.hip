@@ -350,6 +350,58 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
   }
 }
 
+// Norm mode for T within one step: the block loads one sample's Xt tile
+// (rows j0 .. j0 + 127) into LDS once and sweeps a run of column tiles of
+// that sample's dY, writing the same per-(sample, tile, wave) partials as
+// samp_kernel. Xt is read once per run instead of once per column tile.
+template <typename T, bool PAIR>
+__global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a) {
+  typedef MainTile<T> Tl;
+  __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
+  const int lb = xcd_logical_block();
+  if (lb >= a.n_blocks) return;
+  const int li = find_layer(a.L, a.n_layers, lb);
+  const SampLayer& L = a.L[li];
+  const int local = lb - L.block0;
+  const int mt = local % L.m_tiles;
+  const int rest = local / L.m_tiles;
+  const int c = rest % L.n_chunks;  // run of column tiles (runs of one sample
+  const int i = rest / L.n_chunks;  // are neighbours: they share Xt in L2)
+  const int nt0 = c * a.res_tiles, nt1 = min(L.n_tiles, nt0 + a.res_tiles);
+  const int j0 = mt * Tl::BM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = Tl::wave_m(wave), wn = Tl::wave_n(wave);
+  T* sA = smem;
+  T* sB = smem + Tl::BM * Tl::S;
+
+  RowsLoader<T, Tl::BM, Tl::BK, true, IdentityRows> la{a.ldt, a.r - j0, a.T, {}};
+  ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lc{L.d_out, 0, a.T, {}};
+  const T* Xt = static_cast<const T*>(L.Xt) + (static_cast<int64_t>(i) * a.r + j0) * a.ldt;
+  const T* dY = static_cast<const T*>(L.dY) + static_cast<int64_t>(i) * a.T * L.d_out;
+  la.load(Xt, 0, tid, a.off32);
+  lc.ncols = L.d_out - nt0 * Tl::BN;
+  lc.load(dY + nt0 * Tl::BN, 0, tid, a.off32);
+  la.store(sA, tid);
+  Acc<Tl::MB, Tl::NB> acc;
+  acc.zero();
+  for (int nt = nt0; nt < nt1; ++nt) {
+    __syncthreads();  // the previous tile finished reading sB (and sA is written)
+    lc.store(sB, tid);
+    __syncthreads();
+    if (nt + 1 < nt1) {
+      lc.ncols = L.d_out - (nt + 1) * Tl::BN;
+      lc.load(dY + (nt + 1) * Tl::BN, 0, tid, a.off32);
+    }
+    Mma<T, Tl>::run(sA, sB, acc, wm, wn, lane);
+    // Rows and columns outside the layer were loaded as zeros.
+    const float t = wave_sum(acc.sum_sq());
+    if (lane == 0)
+      a.norm_part[static_cast<int64_t>(i) * a.n_slots +
+                  4 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+    acc.zero();
+  }
+}
+
 // ------------------------------------------------------------------ scale --
 
 __global__ __launch_bounds__(kThreads) void scale_kernel(const ScaleArgs a) {
@@ -627,7 +679,15 @@ static hipError_t launch_samp(const SampArgs& a, bool bf16_in, bool pair,
 
 hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
                             hipStream_t s) {
-  return launch_samp<false>(a, bf16_in, pair, s);
+  if (a.res_tiles == 0) return launch_samp<false>(a, bf16_in, pair, s);
+  const dim3 g(grid8(a.n_blocks)), b(kThreads);
+  if (bf16_in) {
+    if (pair) hipLaunchKernelGGL((norm_res_kernel<bf16, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((norm_res_kernel<bf16, false>), g, b, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((norm_res_kernel<float, true>), g, b, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
