@@ -651,6 +651,24 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
     std::memset(&b, 0, sizeof(b));
     b.r = r;
     b.lr = static_cast<float>(lr);
+    // r within one step: each block keeps its P tile and sweeps a run of
+    // column tiles; the run minimises (rounds of resident blocks) x (tiles
+    // per block), ties to the longer run
+    if (ceil_div(r, step_of(dtype)) == 1) {
+      int64_t best = -1, max_nt = 1;
+      for (int l = l0; l < l1; ++l)
+        max_nt = std::max<int64_t>(max_nt, ceil_div(params[l].d_out, kBackN));
+      for (int64_t per = 1; per <= max_nt; ++per) {
+        int64_t nb = 0;
+        for (int l = l0; l < l1; ++l)
+          nb += ceil_div(params[l].d_in, kTileM) * ceil_div(ceil_div(params[l].d_out, kBackN), per);
+        const int64_t cost = ceil_div(nb, target_blocks(dtype)) * per;
+        if (best < 0 || cost <= best) {
+          best = cost;
+          b.res_tiles = static_cast<int32_t>(per);
+        }
+      }
+    }
     blocks = 0;
     bool pair = true;
     for (int l = l0; l < l1; ++l) {
@@ -663,7 +681,12 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
       L.m_tiles = static_cast<int32_t>(ceil_div(params[l].d_in, kTileM));
       L.n_tiles = static_cast<int32_t>(ceil_div(params[l].d_out, kBackN));
       L.block0 = blocks;
-      blocks += L.m_tiles * L.n_tiles;
+      if (b.res_tiles > 0) {
+        L.n_chunks = static_cast<int32_t>(ceil_div(L.n_tiles, b.res_tiles));
+        blocks += L.m_tiles * L.n_chunks;
+      } else {
+        blocks += L.m_tiles * L.n_tiles;
+      }
       // bf16: P and U are gathered two columns (4 bytes) at a time
       pair = pair && params[l].d_in % 2 == 0 && params[l].d_out % 2 == 0;
     }

@@ -168,7 +168,7 @@ struct BackLayer {
   int32_t d_in, d_out;
   int32_t m_tiles, n_tiles;
   int32_t block0;
-  int32_t pad;
+  int32_t n_chunks;   // with res_tiles: runs of column tiles per row tile
 };
 struct BackArgs {
   BackLayer L[kMaxLayers];
@@ -177,6 +177,8 @@ struct BackArgs {
   int32_t r;
   float lr;
   int32_t off32;      // P and U addressable with 32-bit byte offsets
+  int32_t res_tiles;  // r within one step: a block keeps its P tile in LDS
+                      // and sweeps this many column tiles (0: one tile)
 };
 
 // Launchers (dpg_kernels.hip). Each returns the hipError_t of its launch.

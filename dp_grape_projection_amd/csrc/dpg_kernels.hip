@@ -605,6 +605,110 @@ __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
   }
 }
 
+// Back-projection for r within one step: the block keeps its P tile (128
+// rows of d_in) in LDS and sweeps a run of 64-column tiles of W, loading the
+// next tile's W (registers) and U (staged) while the current one runs on the
+// matrix cores.
+template <typename T, bool PAIR>
+__global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a) {
+  typedef BackTile<T> Tl;
+  static_assert(Tl::MB == 1 && Tl::NB == 2, "back tile");
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+  __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
+  const int lb = xcd_logical_block();
+  if (lb >= a.n_blocks) return;
+  const BackLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const int local = lb - L.block0;
+  const int c = local % L.n_chunks, mt = local / L.n_chunks;
+  const int nt0 = c * a.res_tiles, nt1 = min(L.n_tiles, nt0 + a.res_tiles);
+  const int m0 = mt * Tl::BM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = Tl::wave_m(wave), wn = Tl::wave_n(wave);
+  const int lq = Tl::acc_col(0, 0, lane);  // this lane's 2 columns in a tile
+  const bool vec = (L.d_out & 1) == 0;
+  T* sA = smem;
+  T* sB = smem + Tl::BM * Tl::S;
+
+  // W rows of this lane in column tile nt (2 consecutive columns each)
+  auto load_w = [&](int nt, f32x2* w) {
+    const int nq = nt * Tl::BN + lq;
+    if (vec && m0 + Tl::BM <= L.d_in && (nt + 1) * Tl::BN <= L.d_out) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + Tl::acc_row(wm, 0, i, lane);
+        w[i] = *reinterpret_cast<const f32x2*>(L.W + static_cast<int64_t>(m) * L.d_out + nq);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + Tl::acc_row(wm, 0, i, lane);
+      f32x2 x = {0.0f, 0.0f};
+      if (m < L.d_in && nq < L.d_out) {
+        const float* src = L.W + static_cast<int64_t>(m) * L.d_out + nq;
+        if (vec) {
+          x = *reinterpret_cast<const f32x2*>(src);
+        } else {
+          x[0] = src[0];
+          if (nq + 1 < L.d_out) x[1] = src[1];
+        }
+      }
+      w[i] = x;
+    }
+  };
+  auto store_w = [&](int nt, const f32x2* w, const Acc<1, 2>& acc) {
+    const int nq = nt * Tl::BN + lq;
+    const bool full = vec && m0 + Tl::BM <= L.d_in && (nt + 1) * Tl::BN <= L.d_out;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + Tl::acc_row(wm, 0, i, lane);
+      f32x2 x = w[i];
+      x[0] = fmaf(-a.lr, acc.v[0][0][i], x[0]);
+      x[1] = fmaf(-a.lr, acc.v[0][1][i], x[1]);
+      float* dst = L.W + static_cast<int64_t>(m) * L.d_out + nq;
+      if (full) {
+        *reinterpret_cast<f32x2*>(dst) = x;
+      } else if (m < L.d_in && nq < L.d_out) {
+        if (vec) {
+          *reinterpret_cast<f32x2*>(dst) = x;
+        } else {
+          dst[0] = x[0];
+          if (nq + 1 < L.d_out) dst[1] = x[1];
+        }
+      }
+    }
+  };
+
+  ColsLoader<T, Tl::BM, Tl::BK, PAIR, IdentityRows> lp{L.d_in, L.d_in - m0, a.r, {}};
+  ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lu{L.d_out, 0, a.r, {}};
+  const T* U = static_cast<const T*>(L.U);
+  f32x2 w[16], wnext[16];
+  load_w(nt0, w);
+  lp.load(static_cast<const T*>(L.P) + m0, 0, tid, a.off32);
+  lu.ncols = L.d_out - nt0 * Tl::BN;
+  lu.load(U + nt0 * Tl::BN, 0, tid, a.off32);
+  lp.store(sA, tid);
+  Acc<1, 2> acc;
+  for (int nt = nt0; nt < nt1; ++nt) {
+    __syncthreads();  // the previous tile finished reading sB (and sA is written)
+    lu.store(sB, tid);
+    __syncthreads();
+    const bool more = nt + 1 < nt1;
+    if (more) {
+      load_w(nt + 1, wnext);
+      lu.ncols = L.d_out - (nt + 1) * Tl::BN;
+      lu.load(U + (nt + 1) * Tl::BN, 0, tid, a.off32);
+    }
+    acc.zero();
+    Mma<T, Tl>::run(sA, sB, acc, wm, wn, lane);
+    store_w(nt, w, acc);
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = wnext[i];
+    }
+  }
+}
+
 // ---------------------------------------------------------- philox stream --
 
 __global__ __launch_bounds__(kThreads) void philox_normals_kernel(
@@ -716,7 +820,11 @@ hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
 
 hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
-  if (bf16_in) {
+  if (a.res_tiles > 0) {
+    if (!bf16_in) hipLaunchKernelGGL((back_res_kernel<float, true>), g, b, 0, s, a);
+    else if (pair) hipLaunchKernelGGL((back_res_kernel<bf16, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((back_res_kernel<bf16, false>), g, b, 0, s, a);
+  } else if (bf16_in) {
     if (pair) hipLaunchKernelGGL((back_kernel<bf16, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((back_kernel<bf16, false>), g, b, 0, s, a);
   } else {
