@@ -93,14 +93,19 @@ CASES = {
     "wide_unfused_bf16": W.custom_workload("wide_unfused_bf16", 18,
                                            [(64, 17920), (48, 16640)], B=3,
                                            T=8, r=16),
-    # enough tiles x samples that the sum pass adds several samples per
-    # block (groups of 7), each with its own clip factor
+    # many tiles x samples: the sum pass adds several samples per block,
+    # each with its own clip factor
     "groups_bf16": W.custom_workload("groups_bf16", 19,
                                      [(32, 6400), (32, 6400)], B=33, T=8,
                                      r=16),
     "groups_fp32": W.custom_workload("groups_fp32", 20,
                                      [(32, 6400), (32, 6400)], B=33, T=8,
                                      r=16, dtype="fp32"),
+    # fewer tiles: sum groups of 2 samples (accumulator rescaled between
+    # them), with a single-sample last group
+    "groups4_bf16": W.custom_workload("groups4_bf16", 22,
+                                      [(32, 1280), (32, 1280)], B=33, T=8,
+                                      r=16),
 }
 
 
@@ -194,7 +199,8 @@ def test_no_clipping_is_plain_mean():
         assert rel_fro(g, w) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "groups_bf16", "groups_fp32"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "groups_bf16", "groups_fp32",
+                                  "groups4_bf16"])
 def test_mixed_clipping(name):
     """C near the median norm: some samples clipped, some not."""
     wl = CASES[name]
