@@ -478,6 +478,10 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     for (int l = l0; l < l1; ++l)
       if (static_cast<uint64_t>(kTileN) * p.ldp[l] * elem_size(dtype) >= (1ull << 31))
         a.off32 = 0;
+    // every tile and step full: r and B*T whole tiles, d_in whole steps
+    a.full = vec && a.off32 && r % kTileM == 0 && BT % kTileN == 0;
+    for (int l = l0; l < l1; ++l)
+      if (layers[l].d_in % step_of(dtype) != 0) a.full = 0;
     if ((st = timed(K_PROJ, s, [&] { return launch_proj(a, bf16, vec, s); }))) return st;
     if (nx > 0) {
       x.n_layers = nx;

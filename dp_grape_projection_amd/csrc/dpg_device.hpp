@@ -264,9 +264,13 @@ struct RowsLoader {
 
   // off32: every byte offset of the tile from `base` fits in 32 bits (lets
   // a full tile use block-uniform base + 32-bit lane offset addressing).
+  // FULL: the caller guarantees a full tile with off32 (the edge code is not
+  // compiled, which also keeps the loads free of data-dependent branches).
+  template <bool FULL = false>
   __device__ __forceinline__ void load(const T* base, int k0, int tid,
                                        bool off32) {
-    if (VEC && off32 && nrows >= ROWS && k0 + BK <= K) {
+    static_assert(!FULL || VEC, "full tiles use 16-byte loads");
+    if (FULL || (VEC && off32 && nrows >= ROWS && k0 + BK <= K)) {
       const char* bb = reinterpret_cast<const char*>(base);
 #pragma unroll
       for (int p = 0; p < PER; ++p) {

@@ -66,6 +66,7 @@ struct ProjArgs {
   int32_t n_blocks;   // logical blocks (grid is rounded up to a multiple of 8)
   int32_t B, T, r, ldt;
   int32_t off32;      // activation tiles addressable with 32-bit byte offsets
+  int32_t full;       // every tile and step is full, with off32 and 16-byte rows
 };
 
 struct XsumLayer {

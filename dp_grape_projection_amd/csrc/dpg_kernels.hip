@@ -111,7 +111,9 @@ __global__ __launch_bounds__(kThreads) void gen_p_kernel(const GenPArgs a) {
 
 // ------------------------------------------------------------------- proj --
 
-template <typename T, bool VEC>
+// FULL: every tile of the launch is full (see ProjArgs::full); the loads are
+// compiled without their edge code.
+template <typename T, bool VEC, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void proj_kernel(const ProjArgs a) {
   typedef MainTile<T> Tl;
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
@@ -140,8 +142,8 @@ __global__ __launch_bounds__(kThreads, 2) void proj_kernel(const ProjArgs a) {
       la, lx, smem, acc, s_end - s_begin, tid,
       [&](int s) {
         const int k0 = (s_begin + s) * Tl::BK;
-        la.load(Pb, k0, tid, a.off32);
-        lx.load(Ab, k0, tid, a.off32);
+        la.template load<FULL>(Pb, k0, tid, a.off32);
+        lx.template load<FULL>(Ab, k0, tid, a.off32);
       },
       [](int) {});
 
@@ -752,11 +754,13 @@ hipError_t launch_gen_p(const GenPArgs& a, int n_blocks, bool bf16_out,
 hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (bf16_in) {
-    if (vec) hipLaunchKernelGGL((proj_kernel<bf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((proj_kernel<bf16, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((proj_kernel<bf16, true, true>), g, b, 0, s, a);
+    else if (vec) hipLaunchKernelGGL((proj_kernel<bf16, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((proj_kernel<bf16, false, false>), g, b, 0, s, a);
   } else {
-    if (vec) hipLaunchKernelGGL((proj_kernel<float, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((proj_kernel<float, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((proj_kernel<float, true, true>), g, b, 0, s, a);
+    else if (vec) hipLaunchKernelGGL((proj_kernel<float, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((proj_kernel<float, false, false>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
