@@ -533,6 +533,10 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     for (int l = l0; l < l1; ++l)
       if (static_cast<uint64_t>(T) * layers[l].d_out * elem_size(dtype) >= (1ull << 31))
         a.off32 = 0;
+    // every tile and step full: r and d_out whole tiles, T whole steps
+    a.full = *pair && a.off32 && r % kTileM == 0 && T % step_of(dtype) == 0;
+    for (int l = l0; l < l1; ++l)
+      if (layers[l].d_out % kTileN != 0) a.full = 0;
   };
   // 3. squared-norm partials of every (sample, layer, tile)
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
@@ -701,6 +705,10 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
       if (static_cast<uint64_t>(r) * std::max(params[l].d_in, params[l].d_out) *
               elem_size(dtype) >= (1ull << 31))
         b.off32 = 0;
+    // every tile and step full: d_in, d_out whole tiles, r whole steps
+    b.full = pair && b.off32 && r % step_of(dtype) == 0;
+    for (int l = l0; l < l1; ++l)
+      if (params[l].d_in % kTileM != 0 || params[l].d_out % kBackN != 0) b.full = 0;
     if ((st = timed(K_BACK, s, [&] { return launch_back(b, bf16, pair, s); }))) return st;
   }
   return DPG_OK;

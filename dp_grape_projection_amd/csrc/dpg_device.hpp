@@ -341,9 +341,10 @@ struct ColsLoader<bf16, COLS, BK, true, Map> {
   int K;
   uint32_t w[PER][8];
 
+  template <bool FULL = false>
   __device__ __forceinline__ void load(const bf16* base, int k0, int tid,
                                        bool off32) {
-    if (off32 && ncols >= COLS && k0 + BK <= K) {
+    if (FULL || (off32 && ncols >= COLS && k0 + BK <= K)) {
       const char* bb = reinterpret_cast<const char*>(base);
       const uint32_t stride = static_cast<uint32_t>(ld) * 2u;
 #pragma unroll
@@ -410,7 +411,9 @@ struct ColsLoader<bf16, COLS, BK, false, Map> {
   int K;
   uint32_t h[PER][4];  // 8 bf16 packed in pairs
 
+  template <bool FULL = false>
   __device__ __forceinline__ void load(const bf16* base, int k0, int tid, bool) {
+    static_assert(!FULL, "element loads have no full-tile form");
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int it = tid + p * kThreads;
@@ -459,6 +462,7 @@ struct ColsLoader<float, COLS, BK, PAIR, Map> {
   int K;
   f32x4 reg[PER];
 
+  template <bool FULL = false>  // one form for every tile
   __device__ __forceinline__ void load(const float* base, int k0, int tid, bool) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {

@@ -105,6 +105,8 @@ struct SampArgs {
                         // column tiles of its dY (0: runs of samples)
   int32_t n_slots;      // norm mode: partial slots per sample
   int32_t off32;        // one sample's dY addressable with 32-bit byte offsets
+  int32_t full;         // every tile and step full (r, d_out whole tiles, T
+                        // whole steps), with off32 and paired dY columns
   float* norm_part;     // norm mode: [B][n_slots] (sum mode reads it when fused)
   const float* scales;  // sum mode: [B] (unused when fused)
   int32_t fuse_scale;   // sum mode: compute s_i from norm_part in the prologue
@@ -178,6 +180,8 @@ struct BackArgs {
   int32_t r;
   float lr;
   int32_t off32;      // P and U addressable with 32-bit byte offsets
+  int32_t full;       // every tile and step full (d_in, d_out whole tiles, r
+                      // whole steps), with off32 and paired columns
   int32_t res_tiles;  // r within one step: a block keeps its P tile in LDS
                       // and sweeps this many column tiles (0: one tile)
 };

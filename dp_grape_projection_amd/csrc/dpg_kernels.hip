@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
 // rescaled by c / s_i (c = the factor of the previous sample), the sample's
 // product is added by the matrix cores, and the final R is multiplied by the
 // last factor. A sample with s_i = 0 (its norm overflowed) is skipped.
-template <typename T, bool PAIR, bool SUM>
+template <typename T, bool PAIR, bool SUM, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
   typedef MainTile<T> Tl;
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
       la, lc, smem, acc, (i_end - i_begin) * kc, tid,
       [&](int s) {
         const int i = i_begin + s / kc, k0 = (s % kc) * Tl::BK;
-        la.load(Xt + (static_cast<int64_t>(i) * a.r + j0) * a.ldt, k0, tid, a.off32);
-        lc.load(dY + static_cast<int64_t>(i) * a.T * L.d_out + n0, k0, tid, a.off32);
+        la.template load<FULL>(Xt + (static_cast<int64_t>(i) * a.r + j0) * a.ldt, k0, tid, a.off32);
+        lc.template load<FULL>(dY + static_cast<int64_t>(i) * a.T * L.d_out + n0, k0, tid, a.off32);
       },
       [&] {
         if (!SUM || !a.fuse_scale) return;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
 // (rows j0 .. j0 + 127) into LDS once and sweeps a run of column tiles of
 // that sample's dY, writing the same per-(sample, tile, wave) partials as
 // samp_kernel. Xt is read once per run instead of once per column tile.
-template <typename T, bool PAIR>
+template <typename T, bool PAIR, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a) {
   typedef MainTile<T> Tl;
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
@@ -380,9 +380,9 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
   ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lc{L.d_out, 0, a.T, {}};
   const T* Xt = static_cast<const T*>(L.Xt) + (static_cast<int64_t>(i) * a.r + j0) * a.ldt;
   const T* dY = static_cast<const T*>(L.dY) + static_cast<int64_t>(i) * a.T * L.d_out;
-  la.load(Xt, 0, tid, a.off32);
+  la.template load<FULL>(Xt, 0, tid, a.off32);
   lc.ncols = L.d_out - nt0 * Tl::BN;
-  lc.load(dY + nt0 * Tl::BN, 0, tid, a.off32);
+  lc.template load<FULL>(dY + nt0 * Tl::BN, 0, tid, a.off32);
   la.store(sA, tid);
   Acc<Tl::MB, Tl::NB> acc;
   acc.zero();
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
     __syncthreads();
     if (nt + 1 < nt1) {
       lc.ncols = L.d_out - (nt + 1) * Tl::BN;
-      lc.load(dY + (nt + 1) * Tl::BN, 0, tid, a.off32);
+      lc.template load<FULL>(dY + (nt + 1) * Tl::BN, 0, tid, a.off32);
     }
     Mma<T, Tl>::run(sA, sB, acc, wm, wn, lane);
     // Rows and columns outside the layer were loaded as zeros.
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepArgs a) {
 
 template <typename T> using BackTile = Tile<T, kTileM, kBackN, StepK<T>::v, 4, 1>;
 
-template <typename T, bool PAIR>
+template <typename T, bool PAIR, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
   typedef BackTile<T> Tl;
   static_assert(Tl::MB == 1 && Tl::NB == 2, "back tile");
@@ -574,8 +574,8 @@ __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
   run_steps<T, Tl>(
       lp, lu, smem, acc, (a.r + Tl::BK - 1) / Tl::BK, tid,
       [&](int s) {
-        lp.load(Pb, s * Tl::BK, tid, a.off32);
-        lu.load(Ub, s * Tl::BK, tid, a.off32);
+        lp.template load<FULL>(Pb, s * Tl::BK, tid, a.off32);
+        lu.template load<FULL>(Ub, s * Tl::BK, tid, a.off32);
       },
       [](int) {});
 
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
 // rows of d_in) in LDS and sweeps a run of 64-column tiles of W, loading the
 // next tile's W (registers) and U (staged) while the current one runs on the
 // matrix cores.
-template <typename T, bool PAIR>
+template <typename T, bool PAIR, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a) {
   typedef BackTile<T> Tl;
   static_assert(Tl::MB == 1 && Tl::NB == 2, "back tile");
@@ -686,9 +686,9 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
   const T* U = static_cast<const T*>(L.U);
   f32x2 w[16], wnext[16];
   load_w(nt0, w);
-  lp.load(static_cast<const T*>(L.P) + m0, 0, tid, a.off32);
+  lp.template load<FULL>(static_cast<const T*>(L.P) + m0, 0, tid, a.off32);
   lu.ncols = L.d_out - nt0 * Tl::BN;
-  lu.load(U + nt0 * Tl::BN, 0, tid, a.off32);
+  lu.template load<FULL>(U + nt0 * Tl::BN, 0, tid, a.off32);
   lp.store(sA, tid);
   Acc<1, 2> acc;
   for (int nt = nt0; nt < nt1; ++nt) {
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
     if (more) {
       load_w(nt + 1, wnext);
       lu.ncols = L.d_out - (nt + 1) * Tl::BN;
-      lu.load(U + (nt + 1) * Tl::BN, 0, tid, a.off32);
+      lu.template load<FULL>(U + (nt + 1) * Tl::BN, 0, tid, a.off32);
     }
     acc.zero();
     Mma<T, Tl>::run(sA, sB, acc, wm, wn, lane);
@@ -772,15 +772,19 @@ hipError_t launch_xsum(const XsumArgs& a, int n_blocks, bool bf16_out,
   return hipGetLastError();
 }
 
+// FULL (all tiles full, paired columns): the loads are compiled without
+// their edge code.
 template <bool SUM>
 static hipError_t launch_samp(const SampArgs& a, bool bf16_in, bool pair,
                               hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (bf16_in) {
-    if (pair) hipLaunchKernelGGL((samp_kernel<bf16, true, SUM>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((samp_kernel<bf16, false, SUM>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((samp_kernel<bf16, true, SUM, true>), g, b, 0, s, a);
+    else if (pair) hipLaunchKernelGGL((samp_kernel<bf16, true, SUM, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((samp_kernel<bf16, false, SUM, false>), g, b, 0, s, a);
   } else {
-    hipLaunchKernelGGL((samp_kernel<float, true, SUM>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((samp_kernel<float, true, SUM, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((samp_kernel<float, true, SUM, false>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -790,10 +794,12 @@ hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
   if (a.res_tiles == 0) return launch_samp<false>(a, bf16_in, pair, s);
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (bf16_in) {
-    if (pair) hipLaunchKernelGGL((norm_res_kernel<bf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((norm_res_kernel<bf16, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((norm_res_kernel<bf16, true, true>), g, b, 0, s, a);
+    else if (pair) hipLaunchKernelGGL((norm_res_kernel<bf16, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((norm_res_kernel<bf16, false, false>), g, b, 0, s, a);
   } else {
-    hipLaunchKernelGGL((norm_res_kernel<float, true>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((norm_res_kernel<float, true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((norm_res_kernel<float, true, false>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -825,14 +831,23 @@ hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
 hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (a.res_tiles > 0) {
-    if (!bf16_in) hipLaunchKernelGGL((back_res_kernel<float, true>), g, b, 0, s, a);
-    else if (pair) hipLaunchKernelGGL((back_res_kernel<bf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((back_res_kernel<bf16, false>), g, b, 0, s, a);
+    if (!bf16_in) {
+      if (a.full) hipLaunchKernelGGL((back_res_kernel<float, true, true>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((back_res_kernel<float, true, false>), g, b, 0, s, a);
+    } else if (a.full) {
+      hipLaunchKernelGGL((back_res_kernel<bf16, true, true>), g, b, 0, s, a);
+    } else if (pair) {
+      hipLaunchKernelGGL((back_res_kernel<bf16, true, false>), g, b, 0, s, a);
+    } else {
+      hipLaunchKernelGGL((back_res_kernel<bf16, false, false>), g, b, 0, s, a);
+    }
   } else if (bf16_in) {
-    if (pair) hipLaunchKernelGGL((back_kernel<bf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((back_kernel<bf16, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((back_kernel<bf16, true, true>), g, b, 0, s, a);
+    else if (pair) hipLaunchKernelGGL((back_kernel<bf16, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((back_kernel<bf16, false, false>), g, b, 0, s, a);
   } else {
-    hipLaunchKernelGGL((back_kernel<float, true>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((back_kernel<float, true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((back_kernel<float, true, false>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -88,13 +88,13 @@ CASES = {
     "ring_edges_bf16": W.custom_workload("ring_edges_bf16", 21,
                                          [(200, 96), (328, 40)], B=2, T=300,
                                          r=160),
-    # every tile full (r and B*T multiples of 128, d_in a multiple of the
-    # step): the kernels compiled without edge code
+    # every tile and step full (r, B*T, d_in, d_out whole tiles, T and r
+    # whole steps): the kernels compiled without edge code
     "full_tiles_bf16": W.custom_workload("full_tiles_bf16", 23,
-                                         [(256, 192), (384, 128)], B=2, T=64,
+                                         [(256, 256), (384, 128)], B=2, T=128,
                                          r=128),
     "full_tiles_fp32": W.custom_workload("full_tiles_fp32", 24,
-                                         [(64, 96), (96, 160)], B=2, T=64,
+                                         [(128, 256), (256, 128)], B=2, T=64,
                                          r=128, dtype="fp32"),
     # more than 1024 norm partials per sample: clip factors come from the
     # separate scale launch instead of the sum pass's prologue
