@@ -10,8 +10,9 @@ counter (which keys P and the noise) advances every step.
 
 Prints one JSON line: samples/s over the timed steps, the roofline position
 of the dominant kernel (per-kernel times from HIP events recorded on the
-library's stream over a second pass of the same steps), and the CPU oracle's
-rate on the host cores.
+library's stream over a second pass of the same steps), the CPU oracle's
+rate on the host cores, and the rate of the same step in its streaming form
+(dpg_project_layer per layer, then dpg_clip_sum_noise and the update).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mlp4]
 """
@@ -41,6 +42,8 @@ def parse():
                     help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip timing the streaming form of the step")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the steps, copy a buffer of this many MiB "
                          "three times (calibrates HBM byte counters)")
@@ -249,6 +252,33 @@ def main():
                 "mfma_TFLOP/s": dk["TFLOP/s"],
                 "mfma_frac": round(dk["TFLOP/s"] / peak_flops, 4)}
 
+    # The same step in the streaming form (each layer projected on its own,
+    # projections stored, then clip/sum/noise and the update), on the same
+    # inputs; reported beside the main figure.
+    streaming = None
+    if not args.no_streaming:
+        sprep = dpg.PreparedStreamingStep(A, dY, Wd, md, vd, wl.r, wl.clip_C,
+                                          wl.sigma, wl.seed, wl.lr, wl.beta1,
+                                          wl.beta2, wl.eps,
+                                          layer_ids=[L.layer_id for L in wl.layers])
+        for _ in range(args.warmup):
+            step += 1
+            sprep.run(step)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step += 1
+            sprep.run(step)
+        torch.cuda.synchronize()
+        swall = time.perf_counter() - t0
+        hat_bytes = sum(wl.B * wl.r * L.d_out * 4 for L in wl.layers)
+        streaming = {"value": round(wl.B * args.steps / swall, 1), "unit": "samples/s",
+                     "ms_per_step": round(swall * 1e3 / args.steps, 5),
+                     "stored_projection_bytes": hat_bytes}
+        print(f"[bench] streaming form: {swall * 1e6 / args.steps:.1f} us/step",
+              file=sys.stderr, flush=True)
+        del sprep
+
     if args.copy_mb > 0:
         n = args.copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -279,6 +309,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "streaming": streaming,
     }
     print(json.dumps(out), flush=True)
 

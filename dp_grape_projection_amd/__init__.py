@@ -4,8 +4,10 @@ The compute lives in libdpg.so (C ABI in include/dpg.h, HIP kernels in
 csrc/); this package is its thin Python binding.
 """
 from .binding import (  # noqa: F401
-    DPG_BF16, DPG_FP32, DpgError, EXPORTED, LayerGrad, LayerParam, PreparedStep,
-    adam_workspace_size, dpg_adam_backproject, dpg_philox_normals,
-    dpg_project_clip_noise, library_path, load_library,
-    project_workspace_size, timing_enable, timing_read, version,
+    DPG_BF16, DPG_FP32, DpgError, EXPORTED, LayerGrad, LayerHat, LayerParam,
+    PreparedStep, PreparedStreamingStep, adam_workspace_size, dpg_adam_backproject,
+    dpg_clip_sum_noise, dpg_philox_normals, dpg_project_clip_noise,
+    dpg_project_layer, library_path, load_library, project_workspace_size,
+    timing_enable, timing_read, version,
 )
+from .streaming import GrapeOptimizer, ProjectedLinear  # noqa: F401

@@ -29,10 +29,12 @@ DPG_BF16 = 1
 EXPORTED = (
     "dpg_project_workspace_size", "dpg_project_clip_noise",
     "dpg_adam_workspace_size", "dpg_adam_backproject", "dpg_philox_normals",
+    "dpg_project_layer_workspace_size", "dpg_project_layer",
+    "dpg_clip_workspace_size", "dpg_clip_sum_noise",
     "dpg_status_string", "dpg_last_error", "dpg_version",
     "dpg_timing_enable", "dpg_timing_read", "dpg_kernel_name",
 )
-N_KERNEL_KINDS = 9
+N_KERNEL_KINDS = 10
 
 
 class DpgError(RuntimeError):
@@ -45,6 +47,12 @@ class LayerGrad(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64),
                 ("layer_id", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
                 ("A", ctypes.c_void_p), ("dY", ctypes.c_void_p),
+                ("G_priv", ctypes.c_void_p)]
+
+
+class LayerHat(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int64), ("layer_id", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32), ("G_hat", ctypes.c_void_p),
                 ("G_priv", ctypes.c_void_p)]
 
 
@@ -87,6 +95,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         ctypes.POINTER(LayerParam), i32, i32, i32, f64, f64, f64, f64, u64,
         u64, u64, vp, sz, vp]
     lib.dpg_philox_normals.argtypes = [u64, u32, u32, u32, u64, u64, vp, vp, vp]
+    lib.dpg_project_layer_workspace_size.argtypes = [
+        ctypes.POINTER(LayerGrad), i64, i64, i32, i32, ctypes.POINTER(sz)]
+    lib.dpg_project_layer.argtypes = [
+        ctypes.POINTER(LayerGrad), i64, i64, i32, i32, u64, u64, vp, vp, vp, sz, vp]
+    lib.dpg_clip_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
+    lib.dpg_clip_sum_noise.argtypes = [
+        ctypes.POINTER(LayerHat), i32, i64, i32, f64, f64, u64, u64, vp, vp, vp,
+        sz, vp]
     for name in EXPORTED:
         getattr(lib, name).restype = ctypes.c_int
     lib.dpg_status_string.restype = ctypes.c_char_p
@@ -267,6 +283,79 @@ def dpg_adam_backproject(G_priv: Sequence[torch.Tensor], W: Sequence[torch.Tenso
     return W, m, v
 
 
+def dpg_project_layer(A: torch.Tensor, dY: torch.Tensor, r: int, seed: int,
+                      proj_step: int, layer_id: int, norm_sq: torch.Tensor,
+                      G_hat: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Streaming form, one layer (libdpg): G_hat[i] = P A_i^T dY_i
+    ([B, r, d_out] fp32) and norm_sq[i] += ||G_hat[i]||^2. Returns G_hat."""
+    lib = load_library()
+    dt = A.dtype
+    _require(A, "A", dt)
+    _require(dY, "dY", dt)
+    if A.dim() != 3 or dY.dim() != 3 or tuple(A.shape[:2]) != tuple(dY.shape[:2]):
+        raise ValueError("A and dY must be [B, T, d] with common B, T")
+    B, T = int(A.shape[0]), int(A.shape[1])
+    d_in, d_out = int(A.shape[2]), int(dY.shape[2])
+    if G_hat is None:
+        G_hat = torch.empty((B, r, d_out), dtype=torch.float32, device=A.device)
+    _require(G_hat, "G_hat", torch.float32, (B, r, d_out))
+    _require(norm_sq, "norm_sq", torch.float32, (B,))
+    arr = (LayerGrad * 1)()
+    arr[0].d_in, arr[0].d_out, arr[0].layer_id = d_in, d_out, int(layer_id)
+    arr[0].A, arr[0].dY = _ptr(A), _ptr(dY)
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.dpg_project_layer_workspace_size(arr, B, T, int(r), _dtype_code(dt),
+                                                     ctypes.byref(need)))
+    ws, ws_bytes = _workspace(need.value, A.device, workspace)
+    _check(lib, lib.dpg_project_layer(arr, B, T, int(r), _dtype_code(dt), int(seed),
+                                      int(proj_step), _ptr(G_hat), _ptr(norm_sq),
+                                      ws.data_ptr(), ws_bytes, _stream_handle(stream)))
+    return G_hat
+
+
+def dpg_clip_sum_noise(G_hat: Sequence[torch.Tensor], r: int, clip_C: float,
+                       sigma: float, seed: int, step: int, norm_sq: torch.Tensor,
+                       layer_ids: Optional[Sequence[int]] = None,
+                       G_priv: Optional[List[torch.Tensor]] = None,
+                       sample_norms: Optional[torch.Tensor] = None,
+                       return_norms: bool = True,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """Streaming form, after the last layer (libdpg): G_priv_l =
+    (sum_i s_i G_hat_l[i] + sigma C Z_l) / B with s_i from norm_sq.
+    Returns (G_priv list of [r, d_out] fp32, sample norms [B] or None)."""
+    lib = load_library()
+    n = len(G_hat)
+    if n < 1:
+        raise ValueError("G_hat must be a non-empty list")
+    B = int(G_hat[0].shape[0])
+    dev = G_hat[0].device
+    ids = list(range(n)) if layer_ids is None else [int(x) for x in layer_ids]
+    if G_priv is None:
+        G_priv = [torch.empty((r, int(g.shape[2])), dtype=torch.float32, device=dev)
+                  for g in G_hat]
+    if sample_norms is None and return_norms:
+        sample_norms = torch.empty(B, dtype=torch.float32, device=dev)
+    _require(norm_sq, "norm_sq", torch.float32, (B,))
+    arr = (LayerHat * n)()
+    for i in range(n):
+        d_out = int(G_hat[i].shape[2])
+        _require(G_hat[i], f"G_hat[{i}]", torch.float32, (B, r, d_out))
+        _require(G_priv[i], f"G_priv[{i}]", torch.float32, (r, d_out))
+        arr[i].d_out, arr[i].layer_id = d_out, ids[i]
+        arr[i].G_hat, arr[i].G_priv = _ptr(G_hat[i]), _ptr(G_priv[i])
+    if sample_norms is not None:
+        _require(sample_norms, "sample_norms", torch.float32, (B,))
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.dpg_clip_workspace_size(B, ctypes.byref(need)))
+    ws, ws_bytes = _workspace(need.value, dev, workspace)
+    _check(lib, lib.dpg_clip_sum_noise(arr, n, B, int(r), float(clip_C), float(sigma),
+                                       int(seed), int(step), _ptr(norm_sq),
+                                       _ptr(sample_norms), ws.data_ptr(), ws_bytes,
+                                       _stream_handle(stream)))
+    return G_priv, sample_norms
+
+
 def dpg_philox_normals(seed: int, layer_id: int, step_word: int, tag: int,
                        start: int, n: int, device="cuda", words: bool = False,
                        stream=None):
@@ -347,6 +436,69 @@ class PreparedStep:
         _check(lib, lib.dpg_adam_backproject(
             self.params, self.n, self.r, self.dtype_code, lr, b1, b2, eps,
             seed, step, step, self.ws2.data_ptr(), self.ws2_bytes, h))
+
+
+class PreparedStreamingStep(PreparedStep):
+    """The same step in the streaming form: dpg_project_layer for each layer
+    in order (stored projections [B, r, d_out] fp32, squared norms summed
+    over the layers), then dpg_clip_sum_noise and dpg_adam_backproject, with
+    every table, buffer and workspace marshalled once."""
+
+    def __init__(self, A, dY, W, m, v, r, clip_C, sigma, seed, lr, beta1,
+                 beta2, eps, layer_ids=None):
+        super().__init__(A, dY, W, m, v, r, clip_C, sigma, seed, lr, beta1,
+                         beta2, eps, layer_ids=layer_ids)
+        dev = A[0].device
+        self.norm_sq = torch.zeros(self.B, dtype=torch.float32, device=dev)
+        self.G_hat = [torch.empty((self.B, self.r, int(d.shape[2])),
+                                  dtype=torch.float32, device=dev) for d in dY]
+        self.one = []
+        need = 0
+        for i in range(self.n):
+            g = (LayerGrad * 1)()
+            ctypes.memmove(ctypes.addressof(g), ctypes.addressof(self.grads[i]),
+                           ctypes.sizeof(LayerGrad))
+            self.one.append(g)
+            b = ctypes.c_size_t(0)
+            _check(self.lib, self.lib.dpg_project_layer_workspace_size(
+                g, self.B, self.T, self.r, self.dtype_code, ctypes.byref(b)))
+            need = max(need, b.value)
+        self.wsl, self.wsl_bytes = _workspace(need, dev, None)
+        b = ctypes.c_size_t(0)
+        _check(self.lib, self.lib.dpg_clip_workspace_size(self.B, ctypes.byref(b)))
+        self.wsc, self.wsc_bytes = _workspace(b.value, dev, None)
+        self.hats = (LayerHat * self.n)()
+        for i in range(self.n):
+            h = self.hats[i]
+            h.d_out, h.layer_id = self.grads[i].d_out, self.grads[i].layer_id
+            h.G_hat, h.G_priv = self.G_hat[i].data_ptr(), self.G_priv[i].data_ptr()
+
+    def run(self, step: int, stream=None) -> None:
+        C, sigma, seed, lr, b1, b2, eps = self.hyper
+        h = _stream_handle(stream)
+        lib = self.lib
+        with torch.cuda.stream(stream) if stream is not None else _nullctx():
+            self.norm_sq.zero_()
+        for i in range(self.n):
+            _check(lib, lib.dpg_project_layer(
+                self.one[i], self.B, self.T, self.r, self.dtype_code, seed, step,
+                self.G_hat[i].data_ptr(), self.norm_sq.data_ptr(),
+                self.wsl.data_ptr(), self.wsl_bytes, h))
+        _check(lib, lib.dpg_clip_sum_noise(
+            self.hats, self.n, self.B, self.r, C, sigma, seed, step,
+            self.norm_sq.data_ptr(), self.sample_norms.data_ptr(),
+            self.wsc.data_ptr(), self.wsc_bytes, h))
+        _check(lib, lib.dpg_adam_backproject(
+            self.params, self.n, self.r, self.dtype_code, lr, b1, b2, eps,
+            seed, step, step, self.ws2.data_ptr(), self.ws2_bytes, h))
+
+
+class _nullctx:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
 
 
 def timing_enable(on: bool = True) -> None:

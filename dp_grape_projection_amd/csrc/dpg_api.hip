@@ -34,10 +34,10 @@ bool debug_sync() {
 
 // ---- kernel-timing diagnostics (off unless dpg_timing_enable(1))
 enum Kind { K_GEN_P, K_PROJ, K_XSUM, K_NORM, K_SCALE, K_SUM, K_FIN, K_PREP,
-            K_BACK, K_COUNT };
+            K_BACK, K_CLIP, K_COUNT };
 static_assert(K_COUNT == DPG_N_KERNEL_KINDS, "kernel kinds");
 const char* const kKindName[K_COUNT] = {"gen_p", "proj", "xsum", "norm", "scale",
-                                        "sum", "fin", "prep", "back"};
+                                        "sum", "fin", "prep", "back", "clip"};
 struct TimedLaunch {
   int kind;
   hipEvent_t start, stop;
@@ -345,7 +345,7 @@ int fill_gen_p(GenPLayer& L, void* out, int64_t d_in, int64_t ld,
 
 extern "C" {
 
-int dpg_version(void) { return 10000; }
+int dpg_version(void) { return 10100; }
 
 const char* dpg_status_string(int status) {
   switch (status) {
@@ -381,26 +381,36 @@ int dpg_adam_workspace_size(const dpg_layer_param* params, int32_t n_layers,
   return DPG_OK;
 }
 
-int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
-                           int64_t B, int64_t T, int32_t r, int32_t dtype,
-                           double clip_C, double sigma, uint64_t seed,
-                           uint64_t step, uint64_t proj_step,
-                           float* sample_norms, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
-  if (st) return st;
-  for (int i = 0; i < n_layers; ++i)
-    if (!layers[i].A || !layers[i].dY || !layers[i].G_priv)
-      return fail(DPG_ERR_INVALID_ARG,
-                  "NULL data pointer in layer index " + std::to_string(i));
+int check_clip_sigma(double clip_C, double sigma) {
   if (!(clip_C > 0.0))
     return fail(DPG_ERR_INVALID_ARG, "clip_C must be > 0");
   if (!(sigma >= 0.0) || std::isinf(sigma))
     return fail(DPG_ERR_INVALID_ARG, "sigma must be finite and >= 0");
   if (std::isinf(clip_C) && sigma != 0.0)
     return fail(DPG_ERR_INVALID_ARG, "sigma must be 0 when clip_C is infinite");
-  if ((st = check_seed_steps(step, proj_step))) return st;
+  return DPG_OK;
+}
+
+// The projection call. With ghat == nullptr: the whole batch step (norms,
+// clip, sum, noise into each layer's G_priv). With ghat: the streaming form
+// for one layer (its product tiles into ghat, its squared norms added into
+// norm_sq); clip_C, sigma, step and sample_norms are then unused.
+int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
+                 int64_t T, int32_t r, int32_t dtype, double clip_C,
+                 double sigma, uint64_t seed, uint64_t step,
+                 uint64_t proj_step, float* sample_norms, void* workspace,
+                 size_t workspace_bytes, void* stream, float* ghat,
+                 float* norm_sq) {
+  const bool layer_mode = ghat != nullptr;
+  int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
+  if (st) return st;
+  for (int i = 0; i < n_layers; ++i)
+    if (!layers[i].A || !layers[i].dY || (!layer_mode && !layers[i].G_priv))
+      return fail(DPG_ERR_INVALID_ARG,
+                  "NULL data pointer in layer index " + std::to_string(i));
+  if (layer_mode && !norm_sq) return fail(DPG_ERR_INVALID_ARG, "norm_sq is NULL");
+  if (!layer_mode && (st = check_clip_sigma(clip_C, sigma))) return st;
+  if ((st = check_seed_steps(layer_mode ? 1 : step, proj_step))) return st;
   const ProjPlan p = plan_proj(layers, n_layers, B, T, r, dtype);
   if ((st = check_workspace(workspace, workspace_bytes, p.total))) return st;
 
@@ -544,8 +554,13 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     SampArgs a;
     bool pair;
     fill_samp(a, l0, l1, false, &pair);
+    if (layer_mode) a.L[0].ghat = ghat;
     if ((st = timed(K_NORM, s, [&] { return launch_samp_norm(a, bf16, pair, s); })))
       return st;
+  }
+  if (layer_mode) {
+    NormAccArgs a{norm_part, p.n_slots, static_cast<int32_t>(B), norm_sq};
+    return timed(K_CLIP, s, [&] { return launch_norm_acc(a, s); });
   }
   // 4. per-sample norm and clip factor (needs every layer's partials); the
   //    sum pass does it itself when the groups are small
@@ -580,6 +595,101 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
     for (int l = l0; l < l1; ++l) {
       FinLayer& L = f.L[l - l0];
       L.part = reinterpret_cast<const float*>(ws + p.off_part[l]);
+      L.out = layers[l].G_priv;
+      L.n_elem = static_cast<int32_t>(static_cast<int64_t>(r) * layers[l].d_out);
+      L.layer_id = layers[l].layer_id;
+      L.block0 = blocks;
+      blocks += static_cast<int>(ceil_div(ceil_div(L.n_elem, 4), kThreads));
+    }
+    f.n_layers = l1 - l0;
+    if ((st = timed(K_FIN, s, [&] { return launch_fin(f, blocks, s); }))) return st;
+  }
+  return DPG_OK;
+}
+
+int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
+                           int64_t B, int64_t T, int32_t r, int32_t dtype,
+                           double clip_C, double sigma, uint64_t seed,
+                           uint64_t step, uint64_t proj_step,
+                           float* sample_norms, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return project_impl(layers, n_layers, B, T, r, dtype, clip_C, sigma, seed, step,
+                      proj_step, sample_norms, workspace, workspace_bytes, stream,
+                      nullptr, nullptr);
+}
+
+int dpg_project_layer_workspace_size(const dpg_layer_grad* layer, int64_t B,
+                                     int64_t T, int32_t r, int32_t dtype,
+                                     size_t* bytes) {
+  return dpg_project_workspace_size(layer, 1, B, T, r, dtype, bytes);
+}
+
+int dpg_project_layer(const dpg_layer_grad* layer, int64_t B, int64_t T,
+                      int32_t r, int32_t dtype, uint64_t seed,
+                      uint64_t proj_step, float* G_hat, float* norm_sq,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!G_hat) return fail(DPG_ERR_INVALID_ARG, "G_hat is NULL");
+  return project_impl(layer, 1, B, T, r, dtype, 1.0, 0.0, seed, 1, proj_step,
+                      nullptr, workspace, workspace_bytes, stream, G_hat, norm_sq);
+}
+
+int dpg_clip_workspace_size(int64_t B, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 1 || B > (1ll << 30)) return fail(DPG_ERR_INVALID_ARG, "B must be in [1, 2^30]");
+  *bytes = align_up(static_cast<size_t>(B) * 4);
+  return DPG_OK;
+}
+
+int dpg_clip_sum_noise(const dpg_layer_hat* layers, int32_t n_layers,
+                       int64_t B, int32_t r, double clip_C, double sigma,
+                       uint64_t seed, uint64_t step, const float* norm_sq,
+                       float* sample_norms, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!layers) return fail(DPG_ERR_INVALID_ARG, "layers is NULL");
+  if (n_layers < 1 || n_layers > (1 << 20))
+    return fail(DPG_ERR_INVALID_ARG, "n_layers must be in [1, 2^20]");
+  if (B < 1 || B > (1ll << 30) || r < 1)
+    return fail(DPG_ERR_INVALID_ARG, "B must be in [1, 2^30] and r >= 1");
+  if (!norm_sq) return fail(DPG_ERR_INVALID_ARG, "norm_sq is NULL");
+  int st;
+  for (int i = 0; i < n_layers; ++i) {
+    if ((st = check_layer_shape(1, layers[i].d_out, r, i))) return st;
+    if (layers[i].reserved != 0)
+      return fail(DPG_ERR_INVALID_ARG, "reserved field must be 0");
+    if (!layers[i].G_hat || !layers[i].G_priv)
+      return fail(DPG_ERR_INVALID_ARG,
+                  "NULL data pointer in layer index " + std::to_string(i));
+  }
+  if ((st = check_unique_ids(layers, n_layers))) return st;
+  if ((st = check_clip_sigma(clip_C, sigma))) return st;
+  if ((st = check_seed_steps(step, 0))) return st;
+  if ((st = check_workspace(workspace, workspace_bytes, align_up(static_cast<size_t>(B) * 4))))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* scales = static_cast<float*>(workspace);
+  ClipArgs c{norm_sq, static_cast<int32_t>(B), static_cast<float>(clip_C), scales,
+             sample_norms};
+  if ((st = timed(K_CLIP, s, [&] { return launch_clip(c, s); }))) return st;
+  const double noise = sigma == 0.0 ? 0.0 : sigma * clip_C;
+  for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
+    const int l1 = std::min(n_layers, l0 + kMaxLayers);
+    FinArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.weights = scales;
+    f.groups = static_cast<int32_t>(B);
+    f.noise_scale = static_cast<float>(noise);
+    f.inv_B = static_cast<float>(1.0 / static_cast<double>(B));
+    f.k0 = static_cast<uint32_t>(seed);
+    f.k1 = static_cast<uint32_t>(seed >> 32);
+    f.step_word = static_cast<uint32_t>(step);
+    int blocks = 0;
+    for (int l = l0; l < l1; ++l) {
+      FinLayer& L = f.L[l - l0];
+      L.part = layers[l].G_hat;
       L.out = layers[l].G_priv;
       L.n_elem = static_cast<int32_t>(static_cast<int64_t>(r) * layers[l].d_out);
       L.layer_id = layers[l].layer_id;

@@ -93,6 +93,8 @@ struct SampLayer {
   int32_t slot0;      // norm mode: first partial slot of this layer
   int32_t block0;
   int32_t n_chunks;   // norm mode with res_tiles: runs of column tiles per sample
+  float* ghat;        // norm mode, or null: each sample's product tile is also
+                      // stored here, [B][r][d_out] fp32 (streaming form)
 };
 struct SampArgs {
   SampLayer L[kMaxLayers];
@@ -124,7 +126,23 @@ struct ScaleArgs {
   float* norms_out;        // [B] or null
 };
 
-// ---- G_priv = (sum_g part_g + sigma C Z) / B
+// ---- streaming form: norm_sq[i] += sum_k part[i][k] (one layer's partials)
+struct NormAccArgs {
+  const float* norm_part;  // [B][n_slots]
+  int32_t n_slots;
+  int32_t B;
+  float* norm_sq;          // [B], read-modify-write
+};
+// ---- streaming form: n_i = sqrt(norm_sq[i]), s_i = min(1, C / n_i)
+struct ClipArgs {
+  const float* norm_sq;    // [B]
+  int32_t B;
+  float clip_C;
+  float* scales;           // [B]
+  float* norms_out;        // [B] or null
+};
+
+// ---- G_priv = (sum_g w_g part_g + sigma C Z) / B  (w_g = 1 without weights)
 struct FinLayer {
   const float* part;  // [groups][r*d_out]
   float* out;         // [r*d_out]
@@ -135,6 +153,7 @@ struct FinLayer {
 };
 struct FinArgs {
   FinLayer L[kMaxLayers];
+  const float* weights;  // [groups] or null (streaming form: the clip factors)
   int32_t n_layers;
   int32_t groups;
   float noise_scale;  // sigma * C (0: no noise term)
@@ -198,6 +217,8 @@ hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
                            hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, int B, hipStream_t s);
 hipError_t launch_fin(const FinArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_norm_acc(const NormAccArgs& a, hipStream_t s);
+hipError_t launch_clip(const ClipArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
                        hipStream_t s);
 hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s);

@@ -235,6 +235,33 @@ __global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
   }
 }
 
+// Stores a main-tile accumulator (waves 4 x 1, each lane 4 consecutive
+// columns of 16 rows) into dst = [r][d_out], rows j0 .., columns n0 ..;
+// rows >= r and columns >= d_out are skipped.
+template <class Tl>
+__device__ __forceinline__ void store_tile(float* dst, const Acc<Tl::MB, Tl::NB>& acc,
+                                           int r, int d_out, int j0, int n0,
+                                           int wave, int lane) {
+  static_assert(Tl::MB == 1 && Tl::NB == 4 && Tl::WGN == 1, "main tile");
+  const int wm = Tl::wave_m(wave);
+  const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 4 columns
+  const bool vec = (d_out & 3) == 0 && nq + 3 < d_out;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int j = j0 + Tl::acc_row(wm, 0, i, lane);
+    if (j >= r || nq >= d_out) continue;
+    float* p = dst + static_cast<int64_t>(j) * d_out + nq;
+    if (vec) {
+      *reinterpret_cast<f32x4*>(p) =
+          f32x4{acc.v[0][0][i], acc.v[0][1][i], acc.v[0][2][i], acc.v[0][3][i]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (nq + q < d_out) p[q] = acc.v[0][q][i];
+    }
+  }
+}
+
 // ---------------------------------------------------------- norm and sum --
 
 // Norm mode: squared-norm partials of Xt_i dY_i per (sample, tile, wave).
@@ -325,30 +352,16 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
         if (lane == 0)
           a.norm_part[static_cast<int64_t>(i) * a.n_slots +
                       4 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+        if (L.ghat)
+          store_tile<Tl>(L.ghat + static_cast<int64_t>(i) * a.r * L.d_out, acc, a.r,
+                         L.d_out, j0, n0, wave, lane);
         acc.zero();
       });
 
   if (SUM) {
-    static_assert(Tl::MB == 1 && Tl::NB == 4 && Tl::WGN == 1, "sum tile");
     acc.scale(c);
-    const int wm = Tl::wave_m(wave);
-    const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 4 columns
-    float* part = L.part + static_cast<int64_t>(g) * a.r * L.d_out;
-    const bool vec = (L.d_out & 3) == 0 && nq + 3 < L.d_out;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = j0 + Tl::acc_row(wm, 0, i, lane);
-      if (j >= a.r || nq >= L.d_out) continue;
-      float* dst = part + static_cast<int64_t>(j) * L.d_out + nq;
-      if (vec) {
-        *reinterpret_cast<f32x4*>(dst) =
-            f32x4{acc.v[0][0][i], acc.v[0][1][i], acc.v[0][2][i], acc.v[0][3][i]};
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (nq + q < L.d_out) dst[q] = acc.v[0][q][i];
-      }
-    }
+    store_tile<Tl>(L.part + static_cast<int64_t>(g) * a.r * L.d_out, acc, a.r, L.d_out,
+                   j0, n0, wave, lane);
   }
 }
 
@@ -400,6 +413,9 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
     if (lane == 0)
       a.norm_part[static_cast<int64_t>(i) * a.n_slots +
                   4 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+    if (L.ghat)
+      store_tile<Tl>(L.ghat + static_cast<int64_t>(i) * a.r * L.d_out, acc, a.r, L.d_out,
+                     j0, nt * Tl::BN, wave, lane);
     acc.zero();
   }
 }
@@ -435,13 +451,23 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
   }
   if ((L.n_elem & 3) == 0) {
     f32x4 s = *reinterpret_cast<const f32x4*>(L.part + e0);
+    if (a.weights) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] *= a.weights[0];
+    }
     for (int g = 1; g < a.groups; ++g) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(
           L.part + g * static_cast<int64_t>(L.n_elem) + e0);
-      s[0] += v[0];
-      s[1] += v[1];
-      s[2] += v[2];
-      s[3] += v[3];
+      if (a.weights) {
+        const float w = a.weights[g];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] = fmaf(w, v[q], s[q]);
+      } else {
+        s[0] += v[0];
+        s[1] += v[1];
+        s[2] += v[2];
+        s[3] += v[3];
+      }
     }
     f32x4 o;
 #pragma unroll
@@ -454,7 +480,10 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
     const int64_t e = e0 + q;
     if (e < L.n_elem) {
       float s = 0.0f;
-      for (int g = 0; g < a.groups; ++g) s += L.part[g * static_cast<int64_t>(L.n_elem) + e];
+      for (int g = 0; g < a.groups; ++g) {
+        const float v = L.part[g * static_cast<int64_t>(L.n_elem) + e];
+        s = a.weights ? fmaf(a.weights[g], v, s) : s + v;
+      }
       L.out[e] = fmaf(a.noise_scale, z[q], s) * a.inv_B;
     }
   }
@@ -737,6 +766,30 @@ __global__ __launch_bounds__(kThreads) void philox_normals_kernel(
 }
 
 
+// ------------------------------------------------------ streaming form --
+
+// norm_sq[i] += sum of one layer's partials of sample i: one wave per
+// sample, lane l adds slots l, l + 64, ... in order, then a fixed butterfly.
+__global__ __launch_bounds__(kThreads) void norm_acc_kernel(const NormAccArgs a) {
+  const int i = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= a.B) return;
+  const float* p = a.norm_part + static_cast<int64_t>(i) * a.n_slots;
+  float t = 0.0f;
+  for (int k = lane; k < a.n_slots; k += 64) t += p[k];
+  t = wave_sum(t);
+  if (lane == 0) a.norm_sq[i] += t;
+}
+
+// n_i = sqrt(norm_sq[i]), s_i = min(1, C / n_i).
+__global__ __launch_bounds__(kThreads) void clip_kernel(const ClipArgs a) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= a.B) return;
+  const float n = sqrtf(a.norm_sq[i]);
+  a.scales[i] = (n > a.clip_C) ? a.clip_C / n : 1.0f;
+  if (a.norms_out) a.norms_out[i] = n;
+}
+
 // -------------------------------------------------------------- launchers --
 
 static inline unsigned grid8(int n_blocks) {
@@ -811,6 +864,18 @@ hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
 
 hipError_t launch_scale(const ScaleArgs& a, int B, hipStream_t s) {
   hipLaunchKernelGGL(scale_kernel, dim3(B), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_acc(const NormAccArgs& a, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((a.B + kThreads / 64 - 1) / (kThreads / 64));
+  hipLaunchKernelGGL(norm_acc_kernel, dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_clip(const ClipArgs& a, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((a.B + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(clip_kernel, dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -160,6 +160,78 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
                          uint64_t proj_step, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Streaming form (Methodology, closing paragraph: the per-sample gradients
+ * are projected layer by layer during the backward pass; the projected
+ * gradients are then aggregated, clipped and noised).
+ *
+ * A caller that obtains each layer's dY during backward projects that layer
+ * at once with dpg_project_layer, which stores the layer's projected
+ * per-sample gradients Ghat_il and adds their squared norms into a per-sample
+ * buffer; the layer's A and dY can then be freed. After the last layer,
+ * dpg_clip_sum_noise turns the stored projections into G_priv. The result is
+ * that of dpg_project_clip_noise over the same layers, up to the order of
+ * fp32 rounding; the cost is B * r * d_out fp32 of storage per layer (instead
+ * of a second pass over dY).
+ */
+
+/*
+ * dpg_project_layer_workspace_size: bytes of device workspace that
+ * dpg_project_layer needs for this layer (written to *bytes). Validates the
+ * shape arguments; pointers inside `layer` are not read.
+ */
+int dpg_project_layer_workspace_size(const dpg_layer_grad* layer, int64_t B,
+                                     int64_t T, int32_t r, int32_t dtype,
+                                     size_t* bytes);
+
+/*
+ * dpg_project_layer: for one layer and every sample i,
+ *     G_hat[i] = P (A_i^T dY_i)           [r][d_out] fp32, computed as
+ *                                          (A_i P^T)^T dY_i
+ *     norm_sq[i] += ||G_hat[i]||_F^2      (the layer's partials in a fixed
+ *                                          order, added last)
+ * Arguments:
+ *   layer        one descriptor; layer->G_priv is not used (may be NULL)
+ *   B, T, r, dtype, seed, proj_step   as for dpg_project_clip_noise
+ *   G_hat        device out [B][r][d_out] fp32
+ *   norm_sq      device in/out [B] fp32; set it to zero before the first
+ *                layer of a step. Layers that share a norm_sq must be
+ *                enqueued one after another (each call reads and writes it).
+ *   workspace    device scratch of dpg_project_layer_workspace_size bytes,
+ *                256-byte aligned
+ */
+int dpg_project_layer(const dpg_layer_grad* layer, int64_t B, int64_t T,
+                      int32_t r, int32_t dtype, uint64_t seed,
+                      uint64_t proj_step, float* G_hat, float* norm_sq,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* One layer's stored projections for dpg_clip_sum_noise. */
+typedef struct {
+  int64_t d_out;       /* > 0 */
+  uint32_t layer_id;   /* the id the layer was projected with; keys Z */
+  uint32_t reserved;   /* set to 0 */
+  const float* G_hat;  /* device, [B][r][d_out] fp32 from dpg_project_layer */
+  float* G_priv;       /* device out, [r][d_out] fp32 */
+} dpg_layer_hat;
+
+/* dpg_clip_workspace_size: bytes of device workspace dpg_clip_sum_noise
+ * needs for a batch of B samples (written to *bytes). */
+int dpg_clip_workspace_size(int64_t B, size_t* bytes);
+
+/*
+ * dpg_clip_sum_noise: the aggregation, clip and noise of the streaming form.
+ *     n_i = sqrt(norm_sq[i]);   s_i = min(1, C / n_i)
+ *     G_priv_l = (sum_i s_i G_hat_l[i] + sigma * C * Z_l) / B
+ * with the argument rules of dpg_project_clip_noise for clip_C, sigma, seed
+ * and step. norm_sq: device [B] fp32 accumulated by dpg_project_layer over
+ * every layer of the step; sample_norms: device out [B] fp32 or NULL.
+ */
+int dpg_clip_sum_noise(const dpg_layer_hat* layers, int32_t n_layers,
+                       int64_t B, int32_t r, double clip_C, double sigma,
+                       uint64_t seed, uint64_t step, const float* norm_sq,
+                       float* sample_norms, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /*
  * dpg_philox_normals: the random stream both calls draw from, exposed so it
  * can be checked on its own. For e in [start, start + n):
@@ -176,7 +248,7 @@ int dpg_philox_normals(uint64_t seed, uint32_t layer_id, uint32_t step_word,
 
 /*
  * Kernel-timing diagnostics. While enabled (process-wide), every kernel that
- * dpg_project_clip_noise / dpg_adam_backproject enqueue is bracketed by a
+ * the step calls enqueue (both forms) is bracketed by a
  * pair of HIP events recorded on the call's own stream. dpg_timing_read waits
  * for those events, adds each launch's elapsed time to the total of its
  * kernel kind and returns, for kinds 0 .. n_kinds-1, the total milliseconds
@@ -184,7 +256,7 @@ int dpg_philox_normals(uint64_t seed, uint32_t layer_id, uint32_t step_word,
  * reset != 0). Kinds: see dpg_kernel_name; DPG_N_KERNEL_KINDS of them.
  * Enabling adds host work per launch; leave it off when timing whole steps.
  */
-#define DPG_N_KERNEL_KINDS 9
+#define DPG_N_KERNEL_KINDS 10
 int dpg_timing_enable(int on);
 int dpg_timing_read(double* total_ms, int64_t* launches, int32_t n_kinds,
                     int reset);

@@ -8,7 +8,7 @@ import re
 import pytest
 
 import dp_grape_projection_amd as dpg
-from dp_grape_projection_amd.binding import LayerGrad, LayerParam
+from dp_grape_projection_amd.binding import LayerGrad, LayerHat, LayerParam
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dpg.h")
@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     for n in ("dpg_project_clip_noise", "dpg_adam_backproject",
               "dpg_project_workspace_size", "dpg_adam_workspace_size",
               "dpg_philox_normals", "dpg_status_string", "dpg_last_error",
-              "dpg_version"):
+              "dpg_version", "dpg_project_layer", "dpg_clip_sum_noise",
+              "dpg_project_layer_workspace_size", "dpg_clip_workspace_size"):
         assert n in names
     assert sorted(dpg.EXPORTED) == names
 
@@ -40,7 +41,7 @@ def test_header_declares_the_entry_points():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.dpg_version() == 10000
+    assert lib.dpg_version() == 10100
 
 
 def test_struct_layout_matches_header():
@@ -48,6 +49,9 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(LayerGrad) == 8 + 8 + 4 + 4 + 3 * 8
     assert ctypes.sizeof(LayerParam) == 8 + 8 + 4 + 4 + 4 * 8
     assert LayerGrad.A.offset == 24 and LayerParam.G_priv.offset == 24
+    # int64 d_out; u32 layer_id, reserved; two pointers
+    assert ctypes.sizeof(LayerHat) == 8 + 4 + 4 + 2 * 8
+    assert LayerHat.G_hat.offset == 16
 
 
 def _grads(shapes, ids=None, ptr=0x1000):
@@ -171,3 +175,78 @@ def test_philox_rejects_invalid_arguments(lib):
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(FileNotFoundError):
         dpg.load_library(str(tmp_path / "missing.so"))
+
+
+# --- streaming form ----------------------------------------------------------
+
+def _hats(d_outs, ids=None, ptr=0x1000):
+    arr = (LayerHat * len(d_outs))()
+    for i, d in enumerate(d_outs):
+        arr[i].d_out = d
+        arr[i].layer_id = i if ids is None else ids[i]
+        arr[i].G_hat = arr[i].G_priv = ptr
+    return arr
+
+
+def test_streaming_workspace_queries(lib):
+    one = ctypes.c_size_t(0)
+    assert lib.dpg_project_layer_workspace_size(_grads([(768, 3072)]), 32, 128, 128, 1,
+                                                ctypes.byref(one)) == 0
+    assert one.value > 0 and one.value % 256 == 0
+    clip = ctypes.c_size_t(0)
+    assert lib.dpg_clip_workspace_size(32, ctypes.byref(clip)) == 0
+    assert clip.value >= 32 * 4 and clip.value % 256 == 0
+    assert lib.dpg_clip_workspace_size(0, ctypes.byref(clip)) == 1
+
+
+BAD_LAYER = [
+    ("zero batch", dict(B=0)),
+    ("zero r", dict(r=0)),
+    ("bad dtype", dict(dtype=5)),
+    ("proj_step 2^32", dict(proj_step=2 ** 32)),
+    ("null G_hat", dict(ghat=None)),
+    ("null norm_sq", dict(norm_sq=None)),
+    ("null data", dict(ptr=0)),
+]
+
+
+@pytest.mark.parametrize("desc,kw", BAD_LAYER, ids=[d for d, _ in BAD_LAYER])
+def test_project_layer_rejects_invalid_arguments(lib, desc, kw):
+    arr = _grads([(16, 8)], ptr=kw.get("ptr", 0x1000))
+    st = lib.dpg_project_layer(arr, kw.get("B", 2), 3, kw.get("r", 4), kw.get("dtype", 1),
+                               0, kw.get("proj_step", 1), kw.get("ghat", 0x2000),
+                               kw.get("norm_sq", 0x3000), 0x10000, 1 << 30, None)
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG, desc
+    assert lib.dpg_last_error() != b""
+
+
+BAD_CLIP = [
+    ("zero layers", dict(n=0)),
+    ("zero batch", dict(B=0)),
+    ("zero r", dict(r=0)),
+    ("zero C", dict(C=0.0)),
+    ("inf C with noise", dict(C=float("inf"), sigma=1.0)),
+    ("negative sigma", dict(sigma=-1.0)),
+    ("step 0", dict(step=0)),
+    ("duplicate ids", dict(ids=[2, 2])),
+    ("null norm_sq", dict(norm_sq=None)),
+    ("null data", dict(ptr=0)),
+]
+
+
+@pytest.mark.parametrize("desc,kw", BAD_CLIP, ids=[d for d, _ in BAD_CLIP])
+def test_clip_sum_noise_rejects_invalid_arguments(lib, desc, kw):
+    arr = _hats([8, 16], kw.get("ids"), kw.get("ptr", 0x1000))
+    st = lib.dpg_clip_sum_noise(arr, kw.get("n", 2), kw.get("B", 2), kw.get("r", 4),
+                                kw.get("C", 1.0), kw.get("sigma", 0.5), 0,
+                                kw.get("step", 1), kw.get("norm_sq", 0x3000), None,
+                                0x10000, 1 << 30, None)
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG, desc
+
+
+def test_clip_sum_noise_workspace_errors(lib):
+    arr = _hats([8])
+    args = (arr, 1, 64, 4, 1.0, 0.5, 0, 1, 0x3000, None)
+    assert lib.dpg_clip_sum_noise(*args, None, 256, None) == 2
+    assert lib.dpg_clip_sum_noise(*args, 0x10000, 255, None) == 2
+    assert lib.dpg_clip_sum_noise(*args, 0x10010, 256, None) == 2
