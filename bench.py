@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Throughput of the DP-GRAPE private update step on one MI355X.
 
-A step is one pass of the whole path over one batch: dpg_project_clip_noise
-(P generation, projection, per-sample norms, clip, batch sum, noise) then
-dpg_adam_backproject (projected Adam, P regeneration, back-projection into W)
-over every layer of the workload. Inputs (A, dY) are synthetic, seeded, and
-resident in HBM before timing starts; W, m and v evolve in place and the step
-counter (which keys P and the noise) advances every step.
+A step is one pass of the whole path over one batch, one dpg_private_step
+call over every layer of the workload: P generation, projection, per-sample
+norms, clip, batch sum, noise, projected Adam and the back-projection into W.
+Inputs (A, dY) are synthetic, seeded, and resident in HBM before timing
+starts; W, m and v evolve in place and the step counter (which keys P and the
+noise) advances every step.
 
 Prints one JSON line: samples/s over the timed steps, the roofline position
 of the dominant kernel (per-kernel times from HIP events recorded on the
 library's stream over a second pass of the same steps), the CPU oracle's
-rate on the host cores, and the rate of the same step in its streaming form
-(dpg_project_layer per layer, then dpg_clip_sum_noise and the update).
+rate on the host cores, and beside them the rates of the same step as two
+calls (dpg_project_clip_noise then dpg_adam_backproject) and in its
+streaming form (dpg_project_layer per layer, then dpg_clip_sum_noise and the
+update).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mlp4]
 """
@@ -43,7 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-streaming", action="store_true",
-                    help="skip timing the streaming form of the step")
+                    help="skip timing the two-call and streaming forms of "
+                         "the step")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the steps, copy a buffer of this many MiB "
                          "three times (calibrates HBM byte counters)")
@@ -86,7 +89,9 @@ def measured_traffic(kernel, workload):
 
 
 def kernel_work(wl):
-    """Algorithmic bytes and flops of each kernel kind for one step of `wl`.
+    """Algorithmic bytes and flops of each kernel kind for one step of `wl`
+    (the one-call step: P generated once, the moments updated in the pass
+    that forms G_priv).
 
     Bytes count each input the kernel must read once and each output it must
     write once (es = bytes per A/dY element); flops count the multiply-adds of
@@ -105,8 +110,8 @@ def kernel_work(wl):
         w["norm"][1] += 2.0 * B * T * r * do
         w["sum"][0] += B * T * do * es + B * T * r * es
         w["sum"][1] += 2.0 * B * T * r * do
-        w["fin"][0] += 2 * r * do * 4
-        w["prep"][0] += r * do * (5 * 4 + es) + r * di * es
+        # sum partial in; G_priv, m, v out; m, v in; U out in the operand type
+        w["fin"][0] += r * do * (6 * 4 + es)
         w["back"][0] += 8 * di * do + (di + do) * r * es
         w["back"][1] += 2.0 * di * r * do
     w["scale"][0] += B * 4
@@ -252,11 +257,31 @@ def main():
                 "mfma_TFLOP/s": dk["TFLOP/s"],
                 "mfma_frac": round(dk["TFLOP/s"] / peak_flops, 4)}
 
-    # The same step in the streaming form (each layer projected on its own,
-    # projections stored, then clip/sum/noise and the update), on the same
-    # inputs; reported beside the main figure.
-    streaming = None
+    # The same step as two calls, and in the streaming form (each layer
+    # projected on its own, projections stored, then clip/sum/noise and the
+    # update), on the same inputs; reported beside the main figure.
+    streaming = two_call = None
     if not args.no_streaming:
+        tprep = dpg.PreparedStep(A, dY, Wd, md, vd, wl.r, wl.clip_C, wl.sigma,
+                                 wl.seed, wl.lr, wl.beta1, wl.beta2, wl.eps,
+                                 layer_ids=[L.layer_id for L in wl.layers],
+                                 one_call=False)
+        for _ in range(args.warmup):
+            step += 1
+            tprep.run(step)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step += 1
+            tprep.run(step)
+        torch.cuda.synchronize()
+        twall = time.perf_counter() - t0
+        two_call = {"value": round(wl.B * args.steps / twall, 1), "unit": "samples/s",
+                    "ms_per_step": round(twall * 1e3 / args.steps, 5)}
+        print(f"[bench] two-call form: {twall * 1e6 / args.steps:.1f} us/step",
+              file=sys.stderr, flush=True)
+        del tprep
+
         sprep = dpg.PreparedStreamingStep(A, dY, Wd, md, vd, wl.r, wl.clip_C,
                                           wl.sigma, wl.seed, wl.lr, wl.beta1,
                                           wl.beta2, wl.eps,
@@ -309,6 +334,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "two_call": two_call,
         "streaming": streaming,
     }
     print(json.dumps(out), flush=True)

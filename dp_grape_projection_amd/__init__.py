@@ -6,7 +6,7 @@ csrc/); this package is its thin Python binding.
 from .binding import (  # noqa: F401
     DPG_BF16, DPG_FP32, DpgError, EXPORTED, LayerGrad, LayerHat, LayerParam,
     PreparedStep, PreparedStreamingStep, adam_workspace_size, dpg_adam_backproject,
-    dpg_clip_sum_noise, dpg_philox_normals, dpg_project_clip_noise,
+    dpg_clip_sum_noise, dpg_philox_normals, dpg_private_step, dpg_project_clip_noise,
     dpg_project_layer, library_path, load_library, project_workspace_size,
     timing_enable, timing_read, version,
 )

@@ -31,6 +31,7 @@ EXPORTED = (
     "dpg_adam_workspace_size", "dpg_adam_backproject", "dpg_philox_normals",
     "dpg_project_layer_workspace_size", "dpg_project_layer",
     "dpg_clip_workspace_size", "dpg_clip_sum_noise",
+    "dpg_step_workspace_size", "dpg_private_step",
     "dpg_status_string", "dpg_last_error", "dpg_version",
     "dpg_timing_enable", "dpg_timing_read", "dpg_kernel_name",
 )
@@ -100,6 +101,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dpg_project_layer.argtypes = [
         ctypes.POINTER(LayerGrad), i64, i64, i32, i32, u64, u64, vp, vp, vp, sz, vp]
     lib.dpg_clip_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
+    lib.dpg_step_workspace_size.argtypes = [
+        ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, ctypes.POINTER(sz)]
+    lib.dpg_private_step.argtypes = [
+        ctypes.POINTER(LayerGrad), ctypes.POINTER(LayerParam), i32, i64, i64, i32,
+        i32, f64, f64, f64, f64, f64, f64, u64, u64, u64, vp, vp, sz, vp]
     lib.dpg_clip_sum_noise.argtypes = [
         ctypes.POINTER(LayerHat), i32, i64, i32, f64, f64, u64, u64, vp, vp, vp,
         sz, vp]
@@ -283,6 +289,25 @@ def dpg_adam_backproject(G_priv: Sequence[torch.Tensor], W: Sequence[torch.Tenso
     return W, m, v
 
 
+def dpg_private_step(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
+                     W: Sequence[torch.Tensor], m: Sequence[torch.Tensor],
+                     v: Sequence[torch.Tensor], r: int, clip_C: float, sigma: float,
+                     lr: float, beta1: float, beta2: float, eps: float, seed: int,
+                     step: int, proj_step: Optional[int] = None,
+                     layer_ids: Optional[Sequence[int]] = None, stream=None):
+    """The whole step in one call (libdpg): W, m, v updated in place.
+    Returns (G_priv list of [r, d_out] fp32, sample norms [B])."""
+    ps = PreparedStep(A, dY, W, m, v, r, clip_C, sigma, seed, lr, beta1, beta2,
+                      eps, layer_ids=layer_ids)
+    proj_step = step if proj_step is None else proj_step
+    _check(ps.lib, ps.lib.dpg_private_step(
+        ps.grads, ps.params, ps.n, ps.B, ps.T, ps.r, ps.dtype_code, float(clip_C),
+        float(sigma), float(lr), float(beta1), float(beta2), float(eps), int(seed),
+        int(step), int(proj_step), ps.sample_norms.data_ptr(), ps.ws3.data_ptr(),
+        ps.ws3_bytes, _stream_handle(stream)))
+    return ps.G_priv, ps.sample_norms
+
+
 def dpg_project_layer(A: torch.Tensor, dY: torch.Tensor, r: int, seed: int,
                       proj_step: int, layer_id: int, norm_sq: torch.Tensor,
                       G_hat: Optional[torch.Tensor] = None,
@@ -373,16 +398,19 @@ def dpg_philox_normals(seed: int, layer_id: int, step_word: int, tag: int,
 
 
 class PreparedStep:
-    """One DP-GRAPE step (dpg_project_clip_noise then dpg_adam_backproject)
-    with its layer tables and workspaces marshalled once, for callers that
-    repeat the step on the same buffers (a training loop, the bench).
+    """One DP-GRAPE step with its layer tables and workspaces marshalled
+    once, for callers that repeat the step on the same buffers (a training
+    loop, the bench): dpg_private_step, or with one_call=False the two calls
+    dpg_project_clip_noise and dpg_adam_backproject.
 
-    run(step) enqueues both calls on the current stream with
+    run(step) enqueues the step on the current stream with
     step = proj_step = `step`."""
 
     def __init__(self, A, dY, W, m, v, r, clip_C, sigma, seed, lr, beta1,
-                 beta2, eps, layer_ids=None, G_priv=None, sample_norms=None):
+                 beta2, eps, layer_ids=None, G_priv=None, sample_norms=None,
+                 one_call=True):
         self.lib = load_library()
+        self.one_call = one_call
         n = len(A)
         dt = A[0].dtype
         self.dtype_code = _dtype_code(dt)
@@ -423,12 +451,23 @@ class PreparedStep:
             self.params, n, self.r, self.dtype_code, ctypes.byref(need2)))
         self.ws1, self.ws1_bytes = _workspace(need1.value, dev, None)
         self.ws2, self.ws2_bytes = _workspace(need2.value, dev, None)
+        need3 = ctypes.c_size_t(0)
+        _check(self.lib, self.lib.dpg_step_workspace_size(
+            self.grads, n, self.B, self.T, self.r, self.dtype_code,
+            ctypes.byref(need3)))
+        self.ws3, self.ws3_bytes = _workspace(need3.value if one_call else 0, dev, None)
         self._keep = (A, dY, W, m, v)
 
     def run(self, step: int, stream=None) -> None:
         C, sigma, seed, lr, b1, b2, eps = self.hyper
         h = _stream_handle(stream)
         lib = self.lib
+        if self.one_call:
+            _check(lib, lib.dpg_private_step(
+                self.grads, self.params, self.n, self.B, self.T, self.r,
+                self.dtype_code, C, sigma, lr, b1, b2, eps, seed, step, step,
+                self.sample_norms.data_ptr(), self.ws3.data_ptr(), self.ws3_bytes, h))
+            return
         _check(lib, lib.dpg_project_clip_noise(
             self.grads, self.n, self.B, self.T, self.r, self.dtype_code, C,
             sigma, seed, step, step, self.sample_norms.data_ptr(),

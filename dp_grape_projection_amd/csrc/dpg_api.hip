@@ -341,43 +341,97 @@ int fill_gen_p(GenPLayer& L, void* out, int64_t d_in, int64_t ld,
   return static_cast<int>(ceil_div(L.n_ctr, kThreads));
 }
 
-}  // namespace
-
-extern "C" {
-
-int dpg_version(void) { return 10100; }
-
-const char* dpg_status_string(int status) {
-  switch (status) {
-    case DPG_OK: return "DPG_OK";
-    case DPG_ERR_INVALID_ARG: return "DPG_ERR_INVALID_ARG: invalid argument";
-    case DPG_ERR_WORKSPACE: return "DPG_ERR_WORKSPACE: workspace missing, too small or misaligned";
-    case DPG_ERR_UNSUPPORTED: return "DPG_ERR_UNSUPPORTED: unsupported configuration";
-    case DPG_ERR_HIP: return "DPG_ERR_HIP: HIP runtime error";
-    default: return "unknown dpg status";
+// W -= lr P^T U for layers [l0, l1) of `params` (one launch): P_of(l) is
+// layer l's P (row stride ldp_of(l)), U_of(l) its U [r][d_out], in the
+// operand type.
+template <class PF, class LF, class UF>
+int enqueue_back(const dpg_layer_param* params, int l0, int l1, int32_t r,
+                 int32_t dtype, double lr, PF P_of, LF ldp_of, UF U_of,
+                 hipStream_t s) {
+  const bool bf16 = dtype == DPG_BF16;
+  BackArgs b;
+  std::memset(&b, 0, sizeof(b));
+  b.r = r;
+  b.lr = static_cast<float>(lr);
+  // r within one step: each block keeps its P tile and sweeps a run of
+  // column tiles; the run minimises (rounds of resident blocks) x (tiles
+  // per block), ties to the longer run
+  if (ceil_div(r, step_of(dtype)) == 1) {
+    int64_t best = -1, max_nt = 1;
+    for (int l = l0; l < l1; ++l)
+      max_nt = std::max<int64_t>(max_nt, ceil_div(params[l].d_out, kBackN));
+    for (int64_t per = 1; per <= max_nt; ++per) {
+      int64_t nb = 0;
+      for (int l = l0; l < l1; ++l)
+        nb += ceil_div(params[l].d_in, kTileM) * ceil_div(ceil_div(params[l].d_out, kBackN), per);
+      const int64_t cost = ceil_div(nb, target_blocks(dtype)) * per;
+      if (best < 0 || cost <= best) {
+        best = cost;
+        b.res_tiles = static_cast<int32_t>(per);
+      }
+    }
   }
+  int blocks = 0;
+  bool pair = true;
+  for (int l = l0; l < l1; ++l) {
+    BackLayer& L = b.L[l - l0];
+    L.P = P_of(l);
+    L.U = U_of(l);
+    L.ldp = static_cast<int32_t>(ldp_of(l));
+    L.W = params[l].W;
+    L.d_in = static_cast<int32_t>(params[l].d_in);
+    L.d_out = static_cast<int32_t>(params[l].d_out);
+    L.m_tiles = static_cast<int32_t>(ceil_div(params[l].d_in, kTileM));
+    L.n_tiles = static_cast<int32_t>(ceil_div(params[l].d_out, kBackN));
+    L.block0 = blocks;
+    if (b.res_tiles > 0) {
+      L.n_chunks = static_cast<int32_t>(ceil_div(L.n_tiles, b.res_tiles));
+      blocks += L.m_tiles * L.n_chunks;
+    } else {
+      blocks += L.m_tiles * L.n_tiles;
+    }
+    // bf16: P and U are gathered two columns (4 bytes) at a time
+    pair = pair && ldp_of(l) % 2 == 0 && params[l].d_out % 2 == 0;
+  }
+  b.n_layers = l1 - l0;
+  b.n_blocks = blocks;
+  b.off32 = 1;
+  for (int l = l0; l < l1; ++l)
+    if (static_cast<uint64_t>(r) * std::max<int64_t>(ldp_of(l), params[l].d_out) *
+            elem_size(dtype) >= (1ull << 31))
+      b.off32 = 0;
+  // every tile and step full: d_in, d_out whole tiles, r whole steps
+  b.full = pair && b.off32 && r % step_of(dtype) == 0;
+  for (int l = l0; l < l1; ++l)
+    if (params[l].d_in % kTileM != 0 || params[l].d_out % kBackN != 0) b.full = 0;
+  return timed(K_BACK, s, [&] { return launch_back(b, bf16, pair, s); });
 }
 
-const char* dpg_last_error(void) { return g_last_error.c_str(); }
+// Adam and back-projection settings of the one-call step.
+struct StepUpdate {
+  const dpg_layer_param* params;
+  double lr, beta1, beta2, eps;
+};
 
-int dpg_project_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
-                               int64_t B, int64_t T, int32_t r, int32_t dtype,
-                               size_t* bytes) {
-  g_last_error.clear();
-  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
-  const int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
-  if (st) return st;
-  *bytes = plan_proj(layers, n_layers, B, T, r, dtype).total;
-  return DPG_OK;
+// Bytes of the one-call step's U buffers, appended after the projection
+// workspace (offsets relative to its start).
+size_t step_u_bytes(const dpg_layer_grad* layers, int32_t n_layers, int32_t r,
+                    int32_t dtype, size_t base, std::vector<size_t>* off_U) {
+  size_t off = base;
+  for (int l = 0; l < n_layers; ++l) {
+    if (off_U) off_U->push_back(off);
+    off = align_up(off + static_cast<size_t>(r) * layers[l].d_out * elem_size(dtype));
+  }
+  return off - base;
 }
 
-int dpg_adam_workspace_size(const dpg_layer_param* params, int32_t n_layers,
-                            int32_t r, int32_t dtype, size_t* bytes) {
-  g_last_error.clear();
-  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
-  const int st = validate_adam_shapes(params, n_layers, r, dtype);
-  if (st) return st;
-  *bytes = plan_adam(params, n_layers, r, dtype).total;
+int check_adam_hyper(double lr, double beta1, double beta2, double eps) {
+  if (!(lr > 0.0) || std::isinf(lr))
+    return fail(DPG_ERR_INVALID_ARG, "lr must be finite and > 0");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+    return fail(DPG_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
+  if (!(eps > 0.0) || std::isinf(eps))
+    return fail(DPG_ERR_INVALID_ARG, "eps must be finite and > 0");
   return DPG_OK;
 }
 
@@ -395,12 +449,15 @@ int check_clip_sigma(double clip_C, double sigma) {
 // clip, sum, noise into each layer's G_priv). With ghat: the streaming form
 // for one layer (its product tiles into ghat, its squared norms added into
 // norm_sq); clip_C, sigma, step and sample_norms are then unused.
+// With upd (the one-call step): the final stage also runs Adam on G_priv,
+// and the back-projection follows, reading the P this call generated; the
+// U buffers live after the projection workspace.
 int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
                  int64_t T, int32_t r, int32_t dtype, double clip_C,
                  double sigma, uint64_t seed, uint64_t step,
                  uint64_t proj_step, float* sample_norms, void* workspace,
                  size_t workspace_bytes, void* stream, float* ghat,
-                 float* norm_sq) {
+                 float* norm_sq, const StepUpdate* upd = nullptr) {
   const bool layer_mode = ghat != nullptr;
   int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
   if (st) return st;
@@ -412,7 +469,9 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   if (!layer_mode && (st = check_clip_sigma(clip_C, sigma))) return st;
   if ((st = check_seed_steps(layer_mode ? 1 : step, proj_step))) return st;
   const ProjPlan p = plan_proj(layers, n_layers, B, T, r, dtype);
-  if ((st = check_workspace(workspace, workspace_bytes, p.total))) return st;
+  std::vector<size_t> off_U;
+  const size_t u_bytes = upd ? step_u_bytes(layers, n_layers, r, dtype, p.total, &off_U) : 0;
+  if ((st = check_workspace(workspace, workspace_bytes, p.total + u_bytes))) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -602,8 +661,73 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       blocks += static_cast<int>(ceil_div(ceil_div(L.n_elem, 4), kThreads));
     }
     f.n_layers = l1 - l0;
-    if ((st = timed(K_FIN, s, [&] { return launch_fin(f, blocks, s); }))) return st;
+    if (!upd) {
+      if ((st = timed(K_FIN, s, [&] { return launch_fin(f, blocks, s); }))) return st;
+      continue;
+    }
+    // the one-call step: Adam on G_priv in the same pass, then W -= lr P^T U
+    const double t = static_cast<double>(step);
+    f.beta1 = static_cast<float>(upd->beta1);
+    f.beta2 = static_cast<float>(upd->beta2);
+    f.one_m_beta1 = static_cast<float>(1.0 - upd->beta1);
+    f.one_m_beta2 = static_cast<float>(1.0 - upd->beta2);
+    f.bc1 = static_cast<float>(1.0 - std::pow(upd->beta1, t));
+    f.bc2 = static_cast<float>(1.0 - std::pow(upd->beta2, t));
+    f.eps = static_cast<float>(upd->eps);
+    for (int l = l0; l < l1; ++l) {
+      FinLayer& L = f.L[l - l0];
+      L.m = upd->params[l].m;
+      L.v = upd->params[l].v;
+      L.U = ws + off_U[l];
+    }
+    if ((st = timed(K_FIN, s, [&] { return launch_fin_adam(f, blocks, bf16, s); })))
+      return st;
+    if ((st = enqueue_back(upd->params, l0, l1, r, dtype, upd->lr,
+                           [&](int l) { return ws + p.off_P[l]; },
+                           [&](int l) { return p.ldp[l]; },
+                           [&](int l) { return ws + off_U[l]; }, s)))
+      return st;
   }
+  return DPG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dpg_version(void) { return 10100; }
+
+const char* dpg_status_string(int status) {
+  switch (status) {
+    case DPG_OK: return "DPG_OK";
+    case DPG_ERR_INVALID_ARG: return "DPG_ERR_INVALID_ARG: invalid argument";
+    case DPG_ERR_WORKSPACE: return "DPG_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case DPG_ERR_UNSUPPORTED: return "DPG_ERR_UNSUPPORTED: unsupported configuration";
+    case DPG_ERR_HIP: return "DPG_ERR_HIP: HIP runtime error";
+    default: return "unknown dpg status";
+  }
+}
+
+const char* dpg_last_error(void) { return g_last_error.c_str(); }
+
+int dpg_project_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
+                               int64_t B, int64_t T, int32_t r, int32_t dtype,
+                               size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
+  if (st) return st;
+  *bytes = plan_proj(layers, n_layers, B, T, r, dtype).total;
+  return DPG_OK;
+}
+
+int dpg_adam_workspace_size(const dpg_layer_param* params, int32_t n_layers,
+                            int32_t r, int32_t dtype, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = validate_adam_shapes(params, n_layers, r, dtype);
+  if (st) return st;
+  *bytes = plan_adam(params, n_layers, r, dtype).total;
   return DPG_OK;
 }
 
@@ -617,6 +741,45 @@ int dpg_project_clip_noise(const dpg_layer_grad* layers, int32_t n_layers,
   return project_impl(layers, n_layers, B, T, r, dtype, clip_C, sigma, seed, step,
                       proj_step, sample_norms, workspace, workspace_bytes, stream,
                       nullptr, nullptr);
+}
+
+int dpg_step_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
+                            int64_t B, int64_t T, int32_t r, int32_t dtype,
+                            size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
+  if (st) return st;
+  const ProjPlan p = plan_proj(layers, n_layers, B, T, r, dtype);
+  *bytes = p.total + step_u_bytes(layers, n_layers, r, dtype, p.total, nullptr);
+  return DPG_OK;
+}
+
+int dpg_private_step(const dpg_layer_grad* layers, const dpg_layer_param* params,
+                     int32_t n_layers, int64_t B, int64_t T, int32_t r,
+                     int32_t dtype, double clip_C, double sigma, double lr,
+                     double beta1, double beta2, double eps, uint64_t seed,
+                     uint64_t step, uint64_t proj_step, float* sample_norms,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!params) return fail(DPG_ERR_INVALID_ARG, "params is NULL");
+  int st = validate_adam_shapes(params, n_layers, r, dtype);
+  if (st) return st;
+  if (!layers) return fail(DPG_ERR_INVALID_ARG, "layers is NULL");
+  for (int i = 0; i < n_layers; ++i) {
+    if (params[i].d_in != layers[i].d_in || params[i].d_out != layers[i].d_out ||
+        params[i].layer_id != layers[i].layer_id)
+      return fail(DPG_ERR_INVALID_ARG, "params and layers differ at layer index " +
+                                           std::to_string(i));
+    if (!params[i].W || !params[i].m || !params[i].v)
+      return fail(DPG_ERR_INVALID_ARG,
+                  "NULL data pointer in layer index " + std::to_string(i));
+  }
+  if ((st = check_adam_hyper(lr, beta1, beta2, eps))) return st;
+  const StepUpdate upd{params, lr, beta1, beta2, eps};
+  return project_impl(layers, n_layers, B, T, r, dtype, clip_C, sigma, seed, step,
+                      proj_step, sample_norms, workspace, workspace_bytes, stream,
+                      nullptr, nullptr, &upd);
 }
 
 int dpg_project_layer_workspace_size(const dpg_layer_grad* layer, int64_t B,
@@ -714,12 +877,7 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
     if (!params[i].G_priv || !params[i].W || !params[i].m || !params[i].v)
       return fail(DPG_ERR_INVALID_ARG,
                   "NULL data pointer in layer index " + std::to_string(i));
-  if (!(lr > 0.0) || std::isinf(lr))
-    return fail(DPG_ERR_INVALID_ARG, "lr must be finite and > 0");
-  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
-    return fail(DPG_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
-  if (!(eps > 0.0) || std::isinf(eps))
-    return fail(DPG_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if ((st = check_adam_hyper(lr, beta1, beta2, eps))) return st;
   if ((st = check_seed_steps(step, proj_step))) return st;
   const AdamPlan p = plan_adam(params, n_layers, r, dtype);
   if ((st = check_workspace(workspace, workspace_bytes, p.total))) return st;
@@ -765,61 +923,11 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
     if ((st = timed(K_PREP, s, [&] { return launch_prep(a, blocks + pblocks, bf16, s); })))
       return st;
     // 6. W -= lr P^T U
-    BackArgs b;
-    std::memset(&b, 0, sizeof(b));
-    b.r = r;
-    b.lr = static_cast<float>(lr);
-    // r within one step: each block keeps its P tile and sweeps a run of
-    // column tiles; the run minimises (rounds of resident blocks) x (tiles
-    // per block), ties to the longer run
-    if (ceil_div(r, step_of(dtype)) == 1) {
-      int64_t best = -1, max_nt = 1;
-      for (int l = l0; l < l1; ++l)
-        max_nt = std::max<int64_t>(max_nt, ceil_div(params[l].d_out, kBackN));
-      for (int64_t per = 1; per <= max_nt; ++per) {
-        int64_t nb = 0;
-        for (int l = l0; l < l1; ++l)
-          nb += ceil_div(params[l].d_in, kTileM) * ceil_div(ceil_div(params[l].d_out, kBackN), per);
-        const int64_t cost = ceil_div(nb, target_blocks(dtype)) * per;
-        if (best < 0 || cost <= best) {
-          best = cost;
-          b.res_tiles = static_cast<int32_t>(per);
-        }
-      }
-    }
-    blocks = 0;
-    bool pair = true;
-    for (int l = l0; l < l1; ++l) {
-      BackLayer& L = b.L[l - l0];
-      L.P = ws + p.off_P[l];
-      L.U = ws + p.off_U[l];
-      L.W = params[l].W;
-      L.d_in = static_cast<int32_t>(params[l].d_in);
-      L.d_out = static_cast<int32_t>(params[l].d_out);
-      L.m_tiles = static_cast<int32_t>(ceil_div(params[l].d_in, kTileM));
-      L.n_tiles = static_cast<int32_t>(ceil_div(params[l].d_out, kBackN));
-      L.block0 = blocks;
-      if (b.res_tiles > 0) {
-        L.n_chunks = static_cast<int32_t>(ceil_div(L.n_tiles, b.res_tiles));
-        blocks += L.m_tiles * L.n_chunks;
-      } else {
-        blocks += L.m_tiles * L.n_tiles;
-      }
-      // bf16: P and U are gathered two columns (4 bytes) at a time
-      pair = pair && params[l].d_in % 2 == 0 && params[l].d_out % 2 == 0;
-    }
-    b.n_layers = l1 - l0;
-    b.n_blocks = blocks;
-    b.off32 = 1;
-    for (int l = l0; l < l1; ++l)
-      if (static_cast<uint64_t>(r) * std::max(params[l].d_in, params[l].d_out) *
-              elem_size(dtype) >= (1ull << 31))
-        b.off32 = 0;
-    // every tile and step full: d_in, d_out whole tiles, r whole steps
-    b.full = pair && b.off32 && r % step_of(dtype) == 0;
-    for (int l = l0; l < l1; ++l)
-      if (params[l].d_in % kTileM != 0 || params[l].d_out % kBackN != 0) b.full = 0;
-    if ((st = timed(K_BACK, s, [&] { return launch_back(b, bf16, pair, s); }))) return st;
+    if ((st = enqueue_back(params, l0, l1, r, dtype, lr,
+                           [&](int l) { return ws + p.off_P[l]; },
+                           [&](int l) { return params[l].d_in; },
+                           [&](int l) { return ws + p.off_U[l]; }, s)))
+      return st;
   }
   return DPG_OK;
 }

@@ -146,6 +146,9 @@ struct ClipArgs {
 struct FinLayer {
   const float* part;  // [groups][r*d_out]
   float* out;         // [r*d_out]
+  float* m;           // with Adam: [r*d_out] first moment, in place
+  float* v;           // with Adam: [r*d_out] second moment, in place
+  void* U;            // with Adam: [r*d_out] direction, operand type
   int32_t n_elem;     // r * d_out
   uint32_t layer_id;
   int32_t block0;
@@ -159,6 +162,8 @@ struct FinArgs {
   float noise_scale;  // sigma * C (0: no noise term)
   float inv_B;
   uint32_t k0, k1, step_word;
+  // with Adam (the one-call step): constants as in PrepArgs
+  float beta1, beta2, one_m_beta1, one_m_beta2, bc1, bc2, eps;
 };
 
 // ---- update call, first launch: Adam on [r][d_out] (U written row-major in
@@ -184,10 +189,12 @@ struct PrepArgs {
 
 // ---- W -= lr P^T U, reading P [r][d_in] and U [r][d_out] directly
 struct BackLayer {
-  const void* P;      // [r][d_in]
+  const void* P;      // [r][ldp]
   const void* U;      // [r][d_out]
   float* W;           // [d_in][d_out]
   int32_t d_in, d_out;
+  int32_t ldp;        // row stride of P (>= d_in)
+  int32_t pad;
   int32_t m_tiles, n_tiles;
   int32_t block0;
   int32_t n_chunks;   // with res_tiles: runs of column tiles per row tile
@@ -217,6 +224,9 @@ hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
                            hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, int B, hipStream_t s);
 hipError_t launch_fin(const FinArgs& a, int n_blocks, hipStream_t s);
+// fin followed, per element, by the Adam update (m, v in place, U written
+// in bf16 when bf16_out, else fp32)
+hipError_t launch_fin_adam(const FinArgs& a, int n_blocks, bool bf16_out, hipStream_t s);
 hipError_t launch_norm_acc(const NormAccArgs& a, hipStream_t s);
 hipError_t launch_clip(const ClipArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,

@@ -438,6 +438,19 @@ __global__ __launch_bounds__(kThreads) void scale_kernel(const ScaleArgs a) {
 
 // -------------------------------------------------------------------- fin --
 
+// Adam direction of one element with the moments updated in place (H:
+// PrepArgs or FinArgs, which carry the same constants).
+template <class H>
+__device__ __forceinline__ float adam_dir(const H& a, float g, float& m, float& v) {
+  m = fmaf(a.beta1, m, a.one_m_beta1 * g);
+  v = fmaf(a.beta2, v, a.one_m_beta2 * (g * g));
+  return (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
+}
+
+// G_priv = (sum_g w_g part_g + sigma C Z) / B for 4 elements per thread;
+// with ADAM, each element then takes the Adam update (m, v in place, the
+// direction written to U in the operand type T).
+template <typename T, bool ADAM>
 __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
   const int b = blockIdx.x;
   const FinLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
@@ -473,6 +486,21 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = fmaf(a.noise_scale, z[q], s[q]) * a.inv_B;
     *reinterpret_cast<f32x4*>(L.out + e0) = o;
+    if (ADAM) {
+      f32x4 m = *reinterpret_cast<const f32x4*>(L.m + e0);
+      f32x4 v = *reinterpret_cast<const f32x4*>(L.v + e0);
+      float u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float mq = m[q], vq = v[q];
+        u[q] = adam_dir(a, o[q], mq, vq);
+        m[q] = mq;
+        v[q] = vq;
+      }
+      *reinterpret_cast<f32x4*>(L.m + e0) = m;
+      *reinterpret_cast<f32x4*>(L.v + e0) = v;
+      store4<T>(static_cast<T*>(L.U) + e0, u[0], u[1], u[2], u[3]);
+    }
     return;
   }
 #pragma unroll
@@ -484,19 +512,21 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
         const float v = L.part[g * static_cast<int64_t>(L.n_elem) + e];
         s = a.weights ? fmaf(a.weights[g], v, s) : s + v;
       }
-      L.out[e] = fmaf(a.noise_scale, z[q], s) * a.inv_B;
+      const float o = fmaf(a.noise_scale, z[q], s) * a.inv_B;
+      L.out[e] = o;
+      if (ADAM) {
+        float m = L.m[e], v = L.v[e];
+        const float u = adam_dir(a, o, m, v);
+        L.m[e] = m;
+        L.v[e] = v;
+        static_cast<T*>(L.U)[e] = from_float<T>(u);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------- prep --
 
-__device__ __forceinline__ float adam_dir(const PrepArgs& a, float g, float& m,
-                                          float& v) {
-  m = fmaf(a.beta1, m, a.one_m_beta1 * g);
-  v = fmaf(a.beta2, v, a.one_m_beta2 * (g * g));
-  return (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
-}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepArgs a) {
@@ -594,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
     }
   }
 
-  ColsLoader<T, Tl::BM, Tl::BK, PAIR, IdentityRows> lp{L.d_in, L.d_in - m0, a.r, {}};
+  ColsLoader<T, Tl::BM, Tl::BK, PAIR, IdentityRows> lp{L.ldp, L.d_in - m0, a.r, {}};
   ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lu{L.d_out, L.d_out - n0, a.r, {}};
   const T* Pb = static_cast<const T*>(L.P) + m0;
   const T* Ub = static_cast<const T*>(L.U) + n0;
@@ -710,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
     }
   };
 
-  ColsLoader<T, Tl::BM, Tl::BK, PAIR, IdentityRows> lp{L.d_in, L.d_in - m0, a.r, {}};
+  ColsLoader<T, Tl::BM, Tl::BK, PAIR, IdentityRows> lp{L.ldp, L.d_in - m0, a.r, {}};
   ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lu{L.d_out, 0, a.r, {}};
   const T* U = static_cast<const T*>(L.U);
   f32x2 w[16], wnext[16];
@@ -880,7 +910,15 @@ hipError_t launch_clip(const ClipArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fin(const FinArgs& a, int n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL(fin_kernel, dim3(n_blocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((fin_kernel<float, false>), dim3(n_blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fin_adam(const FinArgs& a, int n_blocks, bool bf16_out, hipStream_t s) {
+  if (bf16_out)
+    hipLaunchKernelGGL((fin_kernel<bf16, true>), dim3(n_blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((fin_kernel<float, true>), dim3(n_blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -160,6 +160,29 @@ int dpg_adam_backproject(const dpg_layer_param* params, int32_t n_layers,
                          uint64_t proj_step, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * dpg_step_workspace_size / dpg_private_step: the whole step in one call,
+ * dpg_project_clip_noise followed by dpg_adam_backproject on the same
+ * layers, with P generated once and shared by the projection and the
+ * back-projection, and the noise, the 1/B and the Adam moments of each
+ * element computed in one pass. Results are those of the two calls
+ * (identical arithmetic; G_priv, m, v and W bit for bit).
+ * Arguments: layers and params describe the same layers in the same order
+ * (equal d_in, d_out and layer_id; params[l].G_priv is not read: G_priv is
+ * layers[l].G_priv, written by this call); the remaining arguments follow
+ * dpg_project_clip_noise and dpg_adam_backproject. The operand precision of
+ * P^T U follows dtype.
+ */
+int dpg_step_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
+                            int64_t B, int64_t T, int32_t r, int32_t dtype,
+                            size_t* bytes);
+int dpg_private_step(const dpg_layer_grad* layers, const dpg_layer_param* params,
+                     int32_t n_layers, int64_t B, int64_t T, int32_t r,
+                     int32_t dtype, double clip_C, double sigma, double lr,
+                     double beta1, double beta2, double eps, uint64_t seed,
+                     uint64_t step, uint64_t proj_step, float* sample_norms,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Streaming form (Methodology, closing paragraph: the per-sample gradients
  * are projected layer by layer during the backward pass; the projected

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
               "dpg_project_workspace_size", "dpg_adam_workspace_size",
               "dpg_philox_normals", "dpg_status_string", "dpg_last_error",
               "dpg_version", "dpg_project_layer", "dpg_clip_sum_noise",
-              "dpg_project_layer_workspace_size", "dpg_clip_workspace_size"):
+              "dpg_project_layer_workspace_size", "dpg_clip_workspace_size",
+              "dpg_step_workspace_size", "dpg_private_step"):
         assert n in names
     assert sorted(dpg.EXPORTED) == names
 
@@ -250,3 +251,52 @@ def test_clip_sum_noise_workspace_errors(lib):
     assert lib.dpg_clip_sum_noise(*args, None, 256, None) == 2
     assert lib.dpg_clip_sum_noise(*args, 0x10000, 255, None) == 2
     assert lib.dpg_clip_sum_noise(*args, 0x10010, 256, None) == 2
+
+
+# ------------------------------------------------------ the one-call step --
+
+BAD_STEP = BAD_PROJECT + [
+    ("zero lr", dict(lr=0.0)),
+    ("beta1 = 1", dict(b1=1.0)),
+    ("zero eps", dict(eps=0.0)),
+    ("null params", dict(no_params=True)),
+    ("params d_in differs", dict(pshapes=[(16, 8), (9, 16)])),
+    ("params id differs", dict(pids=[0, 7])),
+    ("null W", dict(pptr=0)),
+]
+
+
+@pytest.mark.parametrize("desc,kw", BAD_STEP, ids=[d for d, _ in BAD_STEP])
+def test_private_step_rejects_invalid_arguments(lib, desc, kw):
+    shapes = kw.get("shapes", [(16, 8), (8, 16)])
+    arr = _grads(shapes, kw.get("ids"), kw.get("ptr", 0x1000))
+    pshapes = kw.get("pshapes", shapes)
+    par = None if kw.get("no_params") else _params(
+        pshapes, kw.get("pids", kw.get("ids")), kw.get("pptr", 0x1000))
+    st = lib.dpg_private_step(
+        arr, par, kw.get("n", len(shapes)), kw.get("B", 2), kw.get("T", 3),
+        kw.get("r", 4), kw.get("dtype", 1), kw.get("C", 1.0), kw.get("sigma", 0.5),
+        kw.get("lr", 1e-3), kw.get("b1", 0.9), kw.get("b2", 0.999),
+        kw.get("eps", 1e-8), 0, kw.get("step", 1), kw.get("proj_step", 1), None,
+        0x10000, 1 << 30, None)
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG, desc
+    assert lib.dpg_last_error() != b""
+
+
+def test_private_step_workspace(lib):
+    """The one-call step needs the projection's workspace plus room for the
+    update direction U of every layer; too little, NULL or misaligned is an
+    error before anything is enqueued."""
+    shapes = [(16, 8), (8, 16)]
+    arr, par = _grads(shapes), _params(shapes)
+    need, proj = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.dpg_step_workspace_size(arr, 2, 2, 3, 4, 1, ctypes.byref(need)) == 0
+    assert lib.dpg_project_workspace_size(arr, 2, 2, 3, 4, 1, ctypes.byref(proj)) == 0
+    # U: [4, 8] and [4, 16] bf16, each 256-byte aligned
+    assert need.value == proj.value + 256 + 256
+    assert lib.dpg_step_workspace_size(arr, 2, 2, 3, 4, 1, None) == 1
+    args = (arr, par, 2, 2, 3, 4, 1, 1.0, 0.5, 1e-3, 0.9, 0.999, 1e-8, 0, 1, 1, None)
+    assert lib.dpg_private_step(*args, None, need.value, None) == 2
+    assert lib.dpg_private_step(*args, 0x10000, need.value - 1, None) == 2
+    assert lib.dpg_private_step(*args, 0x10010, need.value, None) == 2
+    assert b"workspace" in lib.dpg_last_error()
