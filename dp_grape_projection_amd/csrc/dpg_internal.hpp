@@ -16,6 +16,9 @@ constexpr int kMaxLayers = 32;
 // bf16 operands and 32 for fp32 operands.
 constexpr int kTileM = 128, kTileN = 128;
 constexpr int kBackN = 64;  // back-projection: 128 x 64 output tiles
+// Partial sums (sum-pass groups, projection splits) are read this many
+// partials at a time, all loads in flight together.
+constexpr int kSumBatch = 8;
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this
 // many norm partials.
@@ -67,6 +70,7 @@ struct ProjArgs {
   int32_t B, T, r, ldt;
   int32_t off32;      // activation tiles addressable with 32-bit byte offsets
   int32_t full;       // every tile and step is full, with off32 and 16-byte rows
+  int32_t groups2;    // 8-wave blocks: two wave groups split each block's steps
 };
 
 struct XsumLayer {

@@ -113,10 +113,16 @@ __global__ __launch_bounds__(kThreads) void gen_p_kernel(const GenPArgs a) {
 
 // FULL: every tile of the launch is full (see ProjArgs::full); the loads are
 // compiled without their edge code.
-template <typename T, bool VEC, bool FULL>
-__global__ __launch_bounds__(kThreads, 2) void proj_kernel(const ProjArgs a) {
+// NG = 2: the block has two groups of 4 waves that take alternate K steps of
+// the block's range (each with its own LDS tiles), and the second group's
+// accumulator is added into the first's through LDS at the end. This gives
+// 8 waves per block without more split partials.
+template <typename T, bool VEC, bool FULL, int NG>
+__global__ __launch_bounds__(kThreads * NG, 3 - NG) void proj_kernel(const ProjArgs a) {
   typedef MainTile<T> Tl;
-  __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
+  __shared__ __attribute__((aligned(16))) T smem_all[NG * Tl::kLdsElems];
+  const int grp = NG == 1 ? 0 : static_cast<int>(threadIdx.x) / kThreads;
+  T* smem = smem_all + grp * Tl::kLdsElems;
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
@@ -127,10 +133,14 @@ __global__ __launch_bounds__(kThreads, 2) void proj_kernel(const ProjArgs a) {
   const int split = rest / L.n_tiles;
   const int j0 = mt * Tl::BM, n0 = nt * Tl::BN;
   const int BT = a.B * a.T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = static_cast<int>(threadIdx.x) % kThreads, lane = tid & 63, wave = tid >> 6;
   const int n_steps_all = (L.d_in + Tl::BK - 1) / Tl::BK;
   const int s_begin = split * L.steps_per_split;
   const int s_end = min(n_steps_all, s_begin + L.steps_per_split);
+  // this group's steps: s_begin + grp, + NG, ...; both groups run the same
+  // number of iterations (the barriers are shared), the second one's last
+  // one empty when the range is odd (it loads the last real step again)
+  const int n_iter = (s_end - s_begin + NG - 1) / NG;
 
   RowsLoader<T, Tl::BM, Tl::BK, true, IdentityRows> la{L.ldp, a.r - j0, L.d_in, {}};
   RowsLoader<T, Tl::BN, Tl::BK, VEC, BOperandRows<Tl>> lx{L.d_in, BT - n0, L.d_in, {}};
@@ -139,13 +149,34 @@ __global__ __launch_bounds__(kThreads, 2) void proj_kernel(const ProjArgs a) {
   Acc<Tl::MB, Tl::NB> acc;
   acc.zero();
   run_steps<T, Tl>(
-      la, lx, smem, acc, s_end - s_begin, tid,
-      [&](int s) {
-        const int k0 = (s_begin + s) * Tl::BK;
+      la, lx, smem, acc, n_iter, tid,
+      [&](int q) {
+        const int k0 = min(s_begin + q * NG + grp, s_end - 1) * Tl::BK;
         la.template load<FULL>(Pb, k0, tid, a.off32);
         lx.template load<FULL>(Ab, k0, tid, a.off32);
       },
-      [](int) {});
+      [] {}, [&](int q) { return s_begin + q * NG + grp < s_end; }, [](int) {});
+  if constexpr (NG == 2) {
+    // second group's accumulator into the first's, element by element
+    // (thread tid of both groups holds the same elements)
+    float* red = reinterpret_cast<float*>(smem_all);
+    constexpr int kAcc = Tl::MB * Tl::NB * 16;
+    static_assert(kAcc * kThreads * sizeof(float) <= NG * Tl::kLdsElems * sizeof(T),
+                  "LDS holds one group's accumulator");
+    __syncthreads();  // every wave finished its last step's LDS reads
+    if (grp == 1) {
+#pragma unroll
+      for (int nb = 0; nb < Tl::NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[(nb * 16 + i) * kThreads + tid] = acc.v[0][nb][i];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int nb = 0; nb < Tl::NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc.v[0][nb][i] += red[(nb * 16 + i) * kThreads + tid];
+  }
 
   // Each lane owns 4 consecutive columns n (= rows of A) of 16 rows j.
   const int wm = Tl::wave_m(wave);
@@ -213,13 +244,27 @@ __global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
   const float* src = L.part + static_cast<int64_t>(j) * BT + n;
   T* Xt = static_cast<T*>(L.Xt);
   if ((a.T & 3) == 0) {
-    f32x4 s = *reinterpret_cast<const f32x4*>(src);
-    for (int sp = 1; sp < L.splits; ++sp) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + sp * plane);
-      s[0] += v[0];
-      s[1] += v[1];
-      s[2] += v[2];
-      s[3] += v[3];
+    // kSumBatch splits in flight together (index clamped), added in order
+    const int last = L.splits - 1;
+    f32x4 buf[kSumBatch];
+    f32x4 s;
+    for (int s0 = 0; s0 <= last; s0 += kSumBatch) {
+#pragma unroll
+      for (int j = 0; j < kSumBatch; ++j)
+        buf[j] = *reinterpret_cast<const f32x4*>(src + min(s0 + j, last) * plane);
+#pragma unroll
+      for (int j = 0; j < kSumBatch; ++j) {
+        const int sp = s0 + j;
+        if (sp > last) break;
+        if (sp == 0) {
+          s = buf[0];
+        } else {
+          s[0] += buf[j][0];
+          s[1] += buf[j][1];
+          s[2] += buf[j][2];
+          s[3] += buf[j][3];
+        }
+      }
     }
     const int bi = n / a.T, t = n - bi * a.T;
     store4<T>(Xt + (static_cast<int64_t>(bi) * a.r + j) * a.ldt + t, s[0], s[1],
@@ -235,28 +280,32 @@ __global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
   }
 }
 
-// Stores a main-tile accumulator (waves 4 x 1, each lane 4 consecutive
-// columns of 16 rows) into dst = [r][d_out], rows j0 .., columns n0 ..;
-// rows >= r and columns >= d_out are skipped.
+// Stores a tile accumulator with waves 4 x 1 (each lane NB = 4 or 2
+// consecutive columns of 16 rows) into dst = [r][d_out], rows j0 ..,
+// columns n0 ..; rows >= r and columns >= d_out are skipped.
 template <class Tl>
 __device__ __forceinline__ void store_tile(float* dst, const Acc<Tl::MB, Tl::NB>& acc,
                                            int r, int d_out, int j0, int n0,
                                            int wave, int lane) {
-  static_assert(Tl::MB == 1 && Tl::NB == 4 && Tl::WGN == 1, "main tile");
+  constexpr int NB = Tl::NB;
+  static_assert(Tl::MB == 1 && (NB == 4 || NB == 2) && Tl::WGN == 1, "4 x 1 waves");
   const int wm = Tl::wave_m(wave);
-  const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 4 columns
-  const bool vec = (d_out & 3) == 0 && nq + 3 < d_out;
+  const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's NB columns
+  const bool vec = (d_out % NB) == 0 && nq + NB - 1 < d_out;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = j0 + Tl::acc_row(wm, 0, i, lane);
     if (j >= r || nq >= d_out) continue;
     float* p = dst + static_cast<int64_t>(j) * d_out + nq;
     if (vec) {
-      *reinterpret_cast<f32x4*>(p) =
-          f32x4{acc.v[0][0][i], acc.v[0][1][i], acc.v[0][2][i], acc.v[0][3][i]};
+      if constexpr (NB == 4)
+        *reinterpret_cast<f32x4*>(p) =
+            f32x4{acc.v[0][0][i], acc.v[0][1][i], acc.v[0][2][i], acc.v[0][3][i]};
+      else
+        *reinterpret_cast<f32x2*>(p) = f32x2{acc.v[0][0][i], acc.v[0][1][i]};
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NB; ++q)
         if (nq + q < d_out) p[q] = acc.v[0][q][i];
     }
   }
@@ -271,9 +320,9 @@ __device__ __forceinline__ void store_tile(float* dst, const Acc<Tl::MB, Tl::NB>
 // rescaled by c / s_i (c = the factor of the previous sample), the sample's
 // product is added by the matrix cores, and the final R is multiplied by the
 // last factor. A sample with s_i = 0 (its norm overflowed) is skipped.
-template <typename T, bool PAIR, bool SUM, bool FULL>
+template <typename T, int BN, bool PAIR, bool SUM, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
-  typedef MainTile<T> Tl;
+  typedef Tile<T, kTileM, BN, StepK<T>::v, 4, 1> Tl;
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
   __shared__ float s_grp[SUM ? kFuseMaxGroup : 1];
   const int lb = xcd_logical_block();
@@ -458,28 +507,53 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
   const int64_t e0 = 4ll * c;
   if (e0 >= L.n_elem) return;
   float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (a.noise_scale != 0.0f) {
-    const StreamKey key{a.k0, a.k1, a.step_word, 1u};
-    normals_at(key, L.layer_id, static_cast<uint32_t>(c), z);
-  }
   if ((L.n_elem & 3) == 0) {
-    f32x4 s = *reinterpret_cast<const f32x4*>(L.part + e0);
+    // The partials are loaded kSumBatch at a time, all in flight together
+    // (the group index is clamped, not branched on, so that no wait falls
+    // between the loads), with the moments and the noise computed while they
+    // arrive; they are added in group order.
+    const float* part = L.part + e0;
+    const int64_t plane = L.n_elem;
+    const int last = a.groups - 1;
+    f32x4 buf[kSumBatch];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j)
+      buf[j] = *reinterpret_cast<const f32x4*>(part + min(j, last) * plane);
+    f32x4 m, v;
+    if (ADAM) {
+      m = *reinterpret_cast<const f32x4*>(L.m + e0);
+      v = *reinterpret_cast<const f32x4*>(L.v + e0);
+    }
+    if (a.noise_scale != 0.0f) {
+      const StreamKey key{a.k0, a.k1, a.step_word, 1u};
+      normals_at(key, L.layer_id, static_cast<uint32_t>(c), z);
+    }
+    f32x4 s = buf[0];
     if (a.weights) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) s[q] *= a.weights[0];
     }
-    for (int g = 1; g < a.groups; ++g) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(
-          L.part + g * static_cast<int64_t>(L.n_elem) + e0);
-      if (a.weights) {
-        const float w = a.weights[g];
+    for (int g0 = 0; g0 < a.groups; g0 += kSumBatch) {
+      if (g0 > 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s[q] = fmaf(w, v[q], s[q]);
-      } else {
-        s[0] += v[0];
-        s[1] += v[1];
-        s[2] += v[2];
-        s[3] += v[3];
+        for (int j = 0; j < kSumBatch; ++j)
+          buf[j] = *reinterpret_cast<const f32x4*>(part + min(g0 + j, last) * plane);
+      }
+#pragma unroll
+      for (int j = 0; j < kSumBatch; ++j) {
+        const int g = g0 + j;
+        if (g == 0) continue;
+        if (g > last) break;
+        if (a.weights) {
+          const float w = a.weights[g];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s[q] = fmaf(w, buf[j][q], s[q]);
+        } else {
+          s[0] += buf[j][0];
+          s[1] += buf[j][1];
+          s[2] += buf[j][2];
+          s[3] += buf[j][3];
+        }
       }
     }
     f32x4 o;
@@ -487,8 +561,6 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
     for (int q = 0; q < 4; ++q) o[q] = fmaf(a.noise_scale, z[q], s[q]) * a.inv_B;
     *reinterpret_cast<f32x4*>(L.out + e0) = o;
     if (ADAM) {
-      f32x4 m = *reinterpret_cast<const f32x4*>(L.m + e0);
-      f32x4 v = *reinterpret_cast<const f32x4*>(L.v + e0);
       float u[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -502,6 +574,10 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
       store4<T>(static_cast<T*>(L.U) + e0, u[0], u[1], u[2], u[3]);
     }
     return;
+  }
+  if (a.noise_scale != 0.0f) {
+    const StreamKey key{a.k0, a.k1, a.step_word, 1u};
+    normals_at(key, L.layer_id, static_cast<uint32_t>(c), z);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -834,18 +910,24 @@ hipError_t launch_gen_p(const GenPArgs& a, int n_blocks, bool bf16_out,
   return hipGetLastError();
 }
 
-hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
-  const dim3 g(grid8(a.n_blocks)), b(kThreads);
+template <int NG>
+static hipError_t launch_proj_ng(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
+  const dim3 g(grid8(a.n_blocks)), b(kThreads * NG);
   if (bf16_in) {
-    if (a.full) hipLaunchKernelGGL((proj_kernel<bf16, true, true>), g, b, 0, s, a);
-    else if (vec) hipLaunchKernelGGL((proj_kernel<bf16, true, false>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((proj_kernel<bf16, false, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((proj_kernel<bf16, true, true, NG>), g, b, 0, s, a);
+    else if (vec) hipLaunchKernelGGL((proj_kernel<bf16, true, false, NG>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((proj_kernel<bf16, false, false, NG>), g, b, 0, s, a);
   } else {
-    if (a.full) hipLaunchKernelGGL((proj_kernel<float, true, true>), g, b, 0, s, a);
-    else if (vec) hipLaunchKernelGGL((proj_kernel<float, true, false>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((proj_kernel<float, false, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((proj_kernel<float, true, true, NG>), g, b, 0, s, a);
+    else if (vec) hipLaunchKernelGGL((proj_kernel<float, true, false, NG>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((proj_kernel<float, false, false, NG>), g, b, 0, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
+  return a.groups2 ? launch_proj_ng<2>(a, bf16_in, vec, s)
+                   : launch_proj_ng<1>(a, bf16_in, vec, s);
 }
 
 hipError_t launch_xsum(const XsumArgs& a, int n_blocks, bool bf16_out,
@@ -857,24 +939,24 @@ hipError_t launch_xsum(const XsumArgs& a, int n_blocks, bool bf16_out,
 
 // FULL (all tiles full, paired columns): the loads are compiled without
 // their edge code.
-template <bool SUM>
+template <int BN, bool SUM>
 static hipError_t launch_samp(const SampArgs& a, bool bf16_in, bool pair,
                               hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (bf16_in) {
-    if (a.full) hipLaunchKernelGGL((samp_kernel<bf16, true, SUM, true>), g, b, 0, s, a);
-    else if (pair) hipLaunchKernelGGL((samp_kernel<bf16, true, SUM, false>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((samp_kernel<bf16, false, SUM, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((samp_kernel<bf16, BN, true, SUM, true>), g, b, 0, s, a);
+    else if (pair) hipLaunchKernelGGL((samp_kernel<bf16, BN, true, SUM, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((samp_kernel<bf16, BN, false, SUM, false>), g, b, 0, s, a);
   } else {
-    if (a.full) hipLaunchKernelGGL((samp_kernel<float, true, SUM, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((samp_kernel<float, true, SUM, false>), g, b, 0, s, a);
+    if (a.full) hipLaunchKernelGGL((samp_kernel<float, BN, true, SUM, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((samp_kernel<float, BN, true, SUM, false>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
                             hipStream_t s) {
-  if (a.res_tiles == 0) return launch_samp<false>(a, bf16_in, pair, s);
+  if (a.res_tiles == 0) return launch_samp<kTileN, false>(a, bf16_in, pair, s);
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (bf16_in) {
     if (a.full) hipLaunchKernelGGL((norm_res_kernel<bf16, true, true>), g, b, 0, s, a);
@@ -889,7 +971,7 @@ hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
 
 hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
                            hipStream_t s) {
-  return launch_samp<true>(a, bf16_in, pair, s);
+  return launch_samp<kTileN, true>(a, bf16_in, pair, s);
 }
 
 hipError_t launch_scale(const ScaleArgs& a, int B, hipStream_t s) {
