@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--no-streaming", action="store_true",
                     help="skip timing the two-call and streaming forms of "
                          "the step")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw A, dY, W on the GPU (workloads.device_layer_inputs); "
+                         "the default for enc12, dec24 and long1, whose host "
+                         "draws would take minutes. Skips the CPU oracle.")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the steps, copy a buffer of this many MiB "
                          "three times (calibrates HBM byte counters)")
@@ -175,19 +179,32 @@ def main():
     dev = torch.device("cuda:0")
 
     t_gen = time.perf_counter()
-    host = [W.layer_inputs(wl, L) for L in wl.layers]
-    state = [W.initial_state(wl, L) for L in wl.layers]
+    device_inputs = args.device_inputs or wl.name in ("enc12", "dec24", "long1")
+    host = state = None
+    if device_inputs:
+        A, dY, Wd, md, vd = [], [], [], [], []
+        for L in wl.layers:
+            a, d = W.device_layer_inputs(wl, L, dev)
+            w, m, v = W.device_initial_state(wl, L, dev)
+            A.append(a)
+            dY.append(d)
+            Wd.append(w)
+            md.append(m)
+            vd.append(v)
+    else:
+        host = [W.layer_inputs(wl, L) for L in wl.layers]
+        state = [W.initial_state(wl, L) for L in wl.layers]
 
-    def to_dev(x):
-        if wl.dtype == "bf16":
-            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(x).to(dev)
+        def to_dev(x):
+            if wl.dtype == "bf16":
+                return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(x).to(dev)
 
-    A = [to_dev(a) for a, _ in host]
-    dY = [to_dev(d) for _, d in host]
-    Wd = [torch.from_numpy(s[0].copy()).to(dev) for s in state]
-    md = [torch.zeros_like(torch.from_numpy(s[1])).to(dev) for s in state]
-    vd = [torch.zeros_like(torch.from_numpy(s[2])).to(dev) for s in state]
+        A = [to_dev(a) for a, _ in host]
+        dY = [to_dev(d) for _, d in host]
+        Wd = [torch.from_numpy(s[0].copy()).to(dev) for s in state]
+        md = [torch.zeros_like(torch.from_numpy(s[1])).to(dev) for s in state]
+        vd = [torch.zeros_like(torch.from_numpy(s[2])).to(dev) for s in state]
     prep = dpg.PreparedStep(A, dY, Wd, md, vd, wl.r, wl.clip_C, wl.sigma,
                             wl.seed, wl.lr, wl.beta1, wl.beta2, wl.eps,
                             layer_ids=[L.layer_id for L in wl.layers])
@@ -257,6 +274,12 @@ def main():
                 "mfma_TFLOP/s": dk["TFLOP/s"],
                 "mfma_frac": round(dk["TFLOP/s"] / peak_flops, 4)}
 
+    # The whole step against its algorithmic HBM bytes at the HBM peak.
+    step_bytes = sum(b for b, _ in work.values())
+    step_roof = {"algorithmic_bytes": int(step_bytes),
+                 "t_lb_us": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+                 "frac": round(step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)}
+
     # The same step as two calls, and in the streaming form (each layer
     # projected on its own, projections stored, then clip/sum/noise and the
     # update), on the same inputs; reported beside the main figure.
@@ -314,7 +337,7 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and host is not None:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, host, state, args.cpu_reps)
 
@@ -327,11 +350,13 @@ def main():
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-        "data": "synthetic (seeded Gaussian A, dY; Gaussian W)",
+        "data": "synthetic (seeded Gaussian A, dY; Gaussian W%s)" % (
+            ", drawn on the GPU" if device_inputs else ""),
         "config": {"workload": wl.name, "layers": layers, "B": wl.B,
                    "T": wl.T, "r": wl.r, "clip_C": wl.clip_C,
                    "sigma": wl.sigma, "parallelism": "single GPU"},
         "roofline": roof,
+        "step_roofline": step_roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "two_call": two_call,

@@ -241,15 +241,23 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       }
     }
   }
-  // Sum pass: sample groups, each adding one fp32 partial of G_priv (ties:
-  // fewer groups, so fewer partials to add up).
+  // Sum pass: sample groups, each adding one fp32 partial of G_priv that the
+  // final pass reads back. The group size minimises the bytes the chip moves:
+  // (rounds of resident blocks) x (blocks per round) x (operand bytes per
+  // block), plus the partials written and read again (ties: fewer groups).
   {
-    int64_t best = -1;
+    int64_t d_out_sum = 0;
+    for (int l = 0; l < n_layers; ++l) d_out_sum += layers[l].d_out;
+    const double tile_bytes =
+        static_cast<double>(ceil_div(T, BK)) * BK * (kTileM + kTileN) * es;
+    double best = -1.0;
     for (int64_t per = B; per >= 1; --per) {
       const int64_t g = ceil_div(B, per);
-      const int64_t cost = ceil_div(tiles_s * g, target) * per;
-      if (best < 0 || cost < best) {
-        best = cost;
+      const double main = static_cast<double>(ceil_div(tiles_s * g, target)) * target *
+                          per * tile_bytes;
+      const double part = 2.0 * g * r * static_cast<double>(d_out_sum) * 4.0;
+      if (best < 0.0 || main + part < best) {
+        best = main + part;
         p.per_group = static_cast<int32_t>(per);
       }
     }

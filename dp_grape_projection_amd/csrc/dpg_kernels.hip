@@ -228,6 +228,39 @@ __global__ __launch_bounds__(kThreads * NG, 3 - NG) void proj_kernel(const ProjA
   }
 }
 
+// buf[j] = the 16 bytes at src + j * stride for j < n (1 <= n <= kSumBatch),
+// every load issued before any is used: the switch enters a straight run of
+// loads, so no wait falls between them, and no load is repeated.
+__device__ __forceinline__ void load_batch(f32x4 (&buf)[kSumBatch], const float* src,
+                                           int64_t stride, int n) {
+  static_assert(kSumBatch == 8, "one case per batch size");
+  switch (n) {
+    default:
+      buf[7] = *reinterpret_cast<const f32x4*>(src + 7 * stride);
+      [[fallthrough]];
+    case 7:
+      buf[6] = *reinterpret_cast<const f32x4*>(src + 6 * stride);
+      [[fallthrough]];
+    case 6:
+      buf[5] = *reinterpret_cast<const f32x4*>(src + 5 * stride);
+      [[fallthrough]];
+    case 5:
+      buf[4] = *reinterpret_cast<const f32x4*>(src + 4 * stride);
+      [[fallthrough]];
+    case 4:
+      buf[3] = *reinterpret_cast<const f32x4*>(src + 3 * stride);
+      [[fallthrough]];
+    case 3:
+      buf[2] = *reinterpret_cast<const f32x4*>(src + 2 * stride);
+      [[fallthrough]];
+    case 2:
+      buf[1] = *reinterpret_cast<const f32x4*>(src + stride);
+      [[fallthrough]];
+    case 1:
+      buf[0] = *reinterpret_cast<const f32x4*>(src);
+  }
+}
+
 // Xt[b][j][t] = sum over splits of part[s][j][b*T + t]; one thread per 4
 // consecutive n of one row j.
 template <typename T>
@@ -244,14 +277,12 @@ __global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
   const float* src = L.part + static_cast<int64_t>(j) * BT + n;
   T* Xt = static_cast<T*>(L.Xt);
   if ((a.T & 3) == 0) {
-    // kSumBatch splits in flight together (index clamped), added in order
+    // up to kSumBatch splits in flight together, added in split order
     const int last = L.splits - 1;
     f32x4 buf[kSumBatch];
     f32x4 s;
     for (int s0 = 0; s0 <= last; s0 += kSumBatch) {
-#pragma unroll
-      for (int j = 0; j < kSumBatch; ++j)
-        buf[j] = *reinterpret_cast<const f32x4*>(src + min(s0 + j, last) * plane);
+      load_batch(buf, src + s0 * plane, plane, last + 1 - s0);
 #pragma unroll
       for (int j = 0; j < kSumBatch; ++j) {
         const int sp = s0 + j;
@@ -508,17 +539,14 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
   if (e0 >= L.n_elem) return;
   float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if ((L.n_elem & 3) == 0) {
-    // The partials are loaded kSumBatch at a time, all in flight together
-    // (the group index is clamped, not branched on, so that no wait falls
-    // between the loads), with the moments and the noise computed while they
-    // arrive; they are added in group order.
+    // The partials are loaded up to kSumBatch at a time, all in flight
+    // together, with the moments and the noise computed while they arrive;
+    // they are added in group order.
     const float* part = L.part + e0;
     const int64_t plane = L.n_elem;
     const int last = a.groups - 1;
     f32x4 buf[kSumBatch];
-#pragma unroll
-    for (int j = 0; j < kSumBatch; ++j)
-      buf[j] = *reinterpret_cast<const f32x4*>(part + min(j, last) * plane);
+    load_batch(buf, part, plane, a.groups);
     f32x4 m, v;
     if (ADAM) {
       m = *reinterpret_cast<const f32x4*>(L.m + e0);
@@ -534,11 +562,7 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
       for (int q = 0; q < 4; ++q) s[q] *= a.weights[0];
     }
     for (int g0 = 0; g0 < a.groups; g0 += kSumBatch) {
-      if (g0 > 0) {
-#pragma unroll
-        for (int j = 0; j < kSumBatch; ++j)
-          buf[j] = *reinterpret_cast<const f32x4*>(part + min(g0 + j, last) * plane);
-      }
+      if (g0 > 0) load_batch(buf, part + g0 * plane, plane, a.groups - g0);
 #pragma unroll
       for (int j = 0; j < kSumBatch; ++j) {
         const int g = g0 + j;
