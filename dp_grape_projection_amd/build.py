@@ -72,7 +72,7 @@ def _run(cmd, verbose):
                     if "packed-fp32-ops" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"build failed: {' '.join(cmd)}\n{err}")
-    if verbose and err.strip():
+    if err.strip():
         print(err, file=sys.stderr)
 
 

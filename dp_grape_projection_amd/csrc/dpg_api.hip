@@ -57,13 +57,26 @@ struct LaunchTimer {
     std::lock_guard<std::mutex> g(g_timing_mu);
     if (!g_timing_on) return;
     if (hipEventCreate(&start) != hipSuccess) { start = nullptr; return; }
-    hipEventRecord(start, s);
+    if (hipEventRecord(start, s) != hipSuccess) {
+      (void)hipEventDestroy(start);
+      start = nullptr;
+    }
   }
+  // A launch whose events could not be made or recorded is left untimed.
   void done() {
     if (!start) return;
     hipEvent_t stop;
-    if (hipEventCreate(&stop) != hipSuccess) { hipEventDestroy(start); return; }
-    hipEventRecord(stop, s);
+    if (hipEventCreate(&stop) != hipSuccess) {
+      (void)hipEventDestroy(start);
+      start = nullptr;
+      return;
+    }
+    if (hipEventRecord(stop, s) != hipSuccess) {
+      (void)hipEventDestroy(start);
+      (void)hipEventDestroy(stop);
+      start = nullptr;
+      return;
+    }
     std::lock_guard<std::mutex> g(g_timing_mu);
     g_pending.push_back({kind, start, stop});
     start = nullptr;
@@ -968,8 +981,8 @@ int dpg_timing_read(double* total_ms, int64_t* launches, int32_t n_kinds,
       add[t.kind] += ms;
       cnt[t.kind] += 1;
     }
-    hipEventDestroy(t.start);
-    hipEventDestroy(t.stop);
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
   }
   std::lock_guard<std::mutex> g(g_timing_mu);
   for (int k = 0; k < K_COUNT; ++k) {
