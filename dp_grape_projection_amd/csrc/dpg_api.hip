@@ -264,7 +264,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     const double tile_bytes =
         static_cast<double>(ceil_div(T, BK)) * BK * (kTileM + kTileN) * es;
     double best = -1.0;
-    for (int64_t per = B; per >= 1; --per) {
+    for (int64_t per = std::min<int64_t>(B, kSumMaxGroup); per >= 1; --per) {
       const int64_t g = ceil_div(B, per);
       const double main = static_cast<double>(ceil_div(tiles_s * g, target)) * target *
                           per * tile_bytes;

@@ -23,6 +23,8 @@ constexpr int kSumBatch = 8;
 // when a group holds at most this many samples and each sample at most this
 // many norm partials.
 constexpr int kFuseMaxGroup = 64, kFuseMaxSlots = 1024;
+// At most this many samples per sum group (their clip factors sit in LDS).
+constexpr int kSumMaxGroup = 1024;
 constexpr int kStepBf16 = 128, kStepF32 = 32;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }

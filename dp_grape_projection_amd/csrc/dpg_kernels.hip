@@ -355,7 +355,7 @@ template <typename T, int BN, bool PAIR, bool SUM, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
   typedef Tile<T, kTileM, BN, StepK<T>::v, 4, 1> Tl;
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
-  __shared__ float s_grp[SUM ? kFuseMaxGroup : 1];
+  __shared__ float s_grp[SUM ? kSumMaxGroup : 1];  // the group's clip factors
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const int li = find_layer(a.L, a.n_layers, lb);
@@ -388,7 +388,14 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
         lc.template load<FULL>(dY + static_cast<int64_t>(i) * a.T * L.d_out + n0, k0, tid, a.off32);
       },
       [&] {
-        if (!SUM || !a.fuse_scale) return;
+        if (!SUM) return;
+        if (!a.fuse_scale) {
+          // the factors from the scale launch, so that every step reads them
+          // from LDS (a load that may come from global memory would make the
+          // step wait for the next step's prefetched tiles)
+          for (int q = tid; q < i_end - i_begin; q += kThreads) s_grp[q] = a.scales[i_begin + q];
+          return;
+        }
         // Per-sample global norm and clip factor of this group: wave w takes
         // samples w, w + 4, ...; lane l adds slots l, l + 64, ... in order,
         // then the lanes are combined by a fixed butterfly. Every block of
@@ -414,8 +421,7 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
       [&](int s) -> bool {
         if (!SUM) return true;
         if (s % kc == 0) {
-          const int i = i_begin + s / kc;
-          const float si = a.fuse_scale ? s_grp[i - i_begin] : a.scales[i];
+          const float si = s_grp[s / kc];
           on = si > 0.0f;
           if (on) {
             if (c != 0.0f && c != si) acc.scale(c / si);
