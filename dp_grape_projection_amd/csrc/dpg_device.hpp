@@ -27,6 +27,20 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
+// Buffer resource over the 4 GiB from `base`, which must be the same in every
+// lane (it is read from the first one; so are the loader's k0 and ld). The callers keep every offset inside
+// the tensor. Loads through it take one per-lane 32-bit offset plus a
+// block-uniform one, so a tile's loads share one address register and need
+// no 64-bit address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, static_cast<short>(0),
+                                           static_cast<int>(0xFFFFFFFFu), 0x00020000);
+}
+
 // ---------------------------------------------------------------- random --
 
 // Ten Philox rounds: each round multiplies c0 and c2 by the two round
@@ -331,8 +345,12 @@ struct ColsLoader;
 // bf16, PAIR: 32-bit loads (2 columns) from 8 consecutive rows, split into
 // two 8-element k-vectors (needs an even ld, an even column offset of the
 // base and a 4-byte aligned base).
-template <int COLS, int BK, class Map>
-struct ColsLoader<bf16, COLS, BK, true, Map> {
+// BUF: full tiles are read with buffer loads (one lane offset, block-uniform
+// row offsets). This is used where the 64-bit address arithmetic of the plain
+// loads made the compiler wait for a step's first prefetched loads before it
+// issued the rest.
+template <int COLS, int BK, class Map, bool BUF = false>
+struct ColsLoaderPair {
   static constexpr int S = BK + 8;
   static constexpr int ITEMS = (COLS / 2) * (BK / 8);
   static constexpr int PER = ITEMS / kThreads;
@@ -345,6 +363,27 @@ struct ColsLoader<bf16, COLS, BK, true, Map> {
   template <bool FULL = false>
   __device__ __forceinline__ void load(const bf16* base, int k0, int tid,
                                        bool off32) {
+    if constexpr (FULL && BUF) {
+      // item p: columns 2 (tid % (COLS / 2)) + 0..1, rows k0 + 8 (tid /
+      // (COLS / 2) + p kThreads / (COLS / 2)) + j; all but the lane part is
+      // block-uniform
+      static_assert(kThreads % (COLS / 2) == 0, "a thread keeps its column pair");
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base);
+      const uint32_t stride = static_cast<uint32_t>(ld) * 2u;
+      const uint32_t lo = static_cast<uint32_t>(tid / (COLS / 2)) * 8u * stride +
+                          static_cast<uint32_t>(tid % (COLS / 2)) * 4u;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t so = __builtin_amdgcn_readfirstlane(
+              (static_cast<uint32_t>(k0) +
+               static_cast<uint32_t>(p * (kThreads / (COLS / 2)) * 8 + j)) * stride);
+          w[p][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, lo, so, 0);
+        }
+      }
+      return;
+    }
     if (FULL || (off32 && ncols >= COLS && k0 + BK <= K)) {
       const char* bb = reinterpret_cast<const char*>(base);
       const uint32_t stride = static_cast<uint32_t>(ld) * 2u;
@@ -399,6 +438,9 @@ struct ColsLoader<bf16, COLS, BK, true, Map> {
     }
   }
 };
+
+template <int COLS, int BK, class Map>
+struct ColsLoader<bf16, COLS, BK, true, Map> : ColsLoaderPair<COLS, BK, Map, false> {};
 
 // bf16, element loads (odd row stride or unaligned base).
 template <int COLS, int BK, class Map>

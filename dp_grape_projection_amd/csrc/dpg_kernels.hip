@@ -372,7 +372,12 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
   const int kc = (a.T + Tl::BK - 1) / Tl::BK;  // steps per sample
 
   RowsLoader<T, Tl::BM, Tl::BK, true, IdentityRows> la{a.ldt, a.r - j0, a.T, {}};
-  ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>> lc{L.d_out, L.d_out - n0, a.T, {}};
+  // paired bf16 columns: the norm mode reads full tiles with buffer loads
+  typename std::conditional<
+      std::is_same<T, bf16>::value && PAIR,
+      ColsLoaderPair<Tl::BN, Tl::BK, BOperandRows<Tl>, !SUM>,
+      ColsLoader<T, Tl::BN, Tl::BK, PAIR, BOperandRows<Tl>>>::type lc{L.d_out, L.d_out - n0,
+                                                                        a.T, {}};
   const T* Xt = static_cast<const T*>(L.Xt);
   const T* dY = static_cast<const T*>(L.dY);
 
