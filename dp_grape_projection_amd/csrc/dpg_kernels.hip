@@ -709,7 +709,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
   // W rows of this lane (2 consecutive columns each), fetched before the
   // operands so that both are in flight together.
   // interior tile: every row and column in range (block-uniform)
-  const bool full = vec && m0 + Tl::BM <= L.d_in && n0 + Tl::BN <= L.d_out;
+  const bool full = FULL || (vec && m0 + Tl::BM <= L.d_in && n0 + Tl::BN <= L.d_out);
   f32x2 w[16];
   if (full) {
 #pragma unroll
@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
   // W rows of this lane in column tile nt (2 consecutive columns each)
   auto load_w = [&](int nt, f32x2* w) {
     const int nq = nt * Tl::BN + lq;
-    if (vec && m0 + Tl::BM <= L.d_in && (nt + 1) * Tl::BN <= L.d_out) {
+    if (FULL || (vec && m0 + Tl::BM <= L.d_in && (nt + 1) * Tl::BN <= L.d_out)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = m0 + Tl::acc_row(wm, 0, i, lane);
@@ -830,7 +830,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
   };
   auto store_w = [&](int nt, const f32x2* w, const Acc<1, 2>& acc) {
     const int nq = nt * Tl::BN + lq;
-    const bool full = vec && m0 + Tl::BM <= L.d_in && (nt + 1) * Tl::BN <= L.d_out;
+    const bool full = FULL || (vec && m0 + Tl::BM <= L.d_in && (nt + 1) * Tl::BN <= L.d_out);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = m0 + Tl::acc_row(wm, 0, i, lane);
