@@ -572,8 +572,11 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     a.full = vec && a.off32 && r % kTileM == 0 && BT % kTileN == 0;
     for (int l = l0; l < l1; ++l)
       if (layers[l].d_in % step_of(dtype) != 0) a.full = 0;
-    // two wave groups per block: the plan gives about one block per CU
+    // two wave groups per block when every block has at least two K steps
+    // to share (the plan gives about one block per CU)
     a.groups2 = 1;
+    for (int l = l0; l < l1; ++l)
+      if (p.steps_per_split[l] < 2) a.groups2 = 0;
     if ((st = timed(K_PROJ, s, [&] { return launch_proj(a, bf16, vec, s); }))) return st;
     if (nx > 0) {
       x.n_layers = nx;
