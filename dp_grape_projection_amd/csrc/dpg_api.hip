@@ -142,16 +142,23 @@ int check_unique_ids(const L* layers, int32_t n) {
 // run at (their register use allows two 256-thread blocks per CU).
 int64_t target_blocks(int32_t) { return 512; }
 
+#ifndef DPG_PROJ_BIG
+#define DPG_PROJ_BIG 1
+#endif
+constexpr bool kProjBig = DPG_PROJ_BIG != 0;
+
 int step_of(int32_t dtype) { return dtype == DPG_BF16 ? kStepBf16 : kStepF32; }
 
 struct ProjPlan {
   int64_t ldt = 0;             // row stride of Xt (T rounded up to 8)
   std::vector<int64_t> ldp;    // row stride of P per layer
   std::vector<size_t> off_P, off_Xt, off_part, off_xpart;
-  std::vector<int32_t> m_tiles, n_tiles_proj, splits, steps_per_split;
+  std::vector<int32_t> m_tiles;  // per-sample passes: 128-row tiles over r
+  std::vector<int32_t> m_tiles_proj, n_tiles_proj, splits, steps_per_split;  // projection
   std::vector<int32_t> n_tiles_s, slot0;  // per-sample passes: tiles over d_out
   int32_t n_slots = 0;
   int32_t norm_per_block = 1;  // samples per norm block
+  bool big = false;             // projection in proj_big_kernel tiles
   int32_t norm_res_tiles = 0;  // column tiles per norm block (T within one step)
   int32_t groups = 1, per_group = 1;  // sum pass
   bool fuse_scale = false;             // sum pass computes s_i itself
@@ -198,6 +205,40 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     units += mt * ceil_div(BT, kTileN) * ceil_div(layers[l].d_in, BK);
   const int64_t target = target_blocks(dtype);
   const int64_t steps_per_block = std::max<int64_t>(1, ceil_div(units, target / 2));
+  // Large bf16 projections run in 256 x 256 tiles with K steps of 64, one
+  // 8-wave block per CU. The K steps per block minimise an estimate of the
+  // time in steps, max(work / CUs, longest block), plus the split partials
+  // (written and read back) at the bytes one step moves per CU.
+  p.big = kProjBig && dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN;
+  for (int l = 0; l < n_layers; ++l)
+    if (layers[l].d_in % kBigK != 0) p.big = false;
+  int64_t big_sps = 0;
+  if (p.big) {
+    const int64_t tiles = (r / kBigM) * (BT / kBigN), cus = target / 2;
+    int64_t work = 0, max_steps = 1;
+    for (int l = 0; l < n_layers; ++l) {
+      work += tiles * (layers[l].d_in / kBigK);
+      max_steps = std::max<int64_t>(max_steps, layers[l].d_in / kBigK);
+    }
+    double best = -1.0;
+    for (int64_t sps = max_steps; sps >= 1; --sps) {
+      int64_t blocks = 0, longest = 0;
+      double part = 0.0;
+      for (int l = 0; l < n_layers; ++l) {
+        const int64_t steps = layers[l].d_in / kBigK, sp = ceil_div(steps, sps);
+        blocks += tiles * sp;
+        longest = std::max<int64_t>(longest, ceil_div(steps, sp));
+        if (sp > 1) part += 2.0 * sp * r * BT * 4;
+      }
+      const double t = static_cast<double>(blocks <= cus ? longest
+                                                         : std::max(ceil_div(work, cus), longest)) +
+                       part / (static_cast<double>(kBigM + kBigN) * kBigK * 2 * cus);
+      if (best < 0.0 || t < best) {
+        best = t;
+        big_sps = sps;
+      }
+    }
+  }
   size_t off = 0;
   int64_t tiles_s = 0;
   for (int l = 0; l < n_layers; ++l) {
@@ -207,12 +248,13 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     off = align_up(off + static_cast<size_t>(r) * ldp * es);
     p.off_Xt.push_back(off);
     off = align_up(off + static_cast<size_t>(B) * r * p.ldt * es);
-    const int64_t nsteps = ceil_div(layers[l].d_in, BK);
-    int64_t splits = ceil_div(nsteps, steps_per_block);
+    const int64_t nsteps = p.big ? layers[l].d_in / kBigK : ceil_div(layers[l].d_in, BK);
+    int64_t splits = ceil_div(nsteps, p.big ? big_sps : steps_per_block);
     const int64_t sps = ceil_div(nsteps, splits);
     splits = ceil_div(nsteps, sps);
     p.m_tiles.push_back(mt);
-    p.n_tiles_proj.push_back(static_cast<int32_t>(ceil_div(BT, kTileN)));
+    p.m_tiles_proj.push_back(p.big ? static_cast<int32_t>(r / kBigM) : mt);
+    p.n_tiles_proj.push_back(static_cast<int32_t>(p.big ? BT / kBigN : ceil_div(BT, kTileN)));
     p.splits.push_back(static_cast<int32_t>(splits));
     p.steps_per_split.push_back(static_cast<int32_t>(sps));
     p.off_xpart.push_back(off);
@@ -545,7 +587,7 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       L.part = reinterpret_cast<float*>(ws + p.off_xpart[l]);
       L.d_in = static_cast<int32_t>(layers[l].d_in);
       L.ldp = static_cast<int32_t>(p.ldp[l]);
-      L.m_tiles = p.m_tiles[l];
+      L.m_tiles = p.m_tiles_proj[l];
       L.n_tiles = p.n_tiles_proj[l];
       L.splits = p.splits[l];
       L.steps_per_split = p.steps_per_split[l];
@@ -563,6 +605,29 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     }
     a.n_layers = l1 - l0;
     a.n_blocks = blocks;
+    if (p.big) {
+      // the direct copies need 16-byte aligned rows of A; otherwise the
+      // regular kernel runs these layers unsplit (no partials are needed)
+      a.big = 1;
+      for (int l = l0; l < l1; ++l)
+        if (!aligned(layers[l].A, 16)) a.big = 0;
+      if (!a.big) {
+        blocks = 0;
+        nx = 0;
+        xblocks = 0;
+        const int64_t BK = step_of(dtype);
+        for (int l = l0; l < l1; ++l) {
+          ProjLayer& L = a.L[l - l0];
+          L.m_tiles = static_cast<int32_t>(ceil_div(r, kTileM));
+          L.n_tiles = static_cast<int32_t>(ceil_div(BT, kTileN));
+          L.splits = 1;
+          L.steps_per_split = static_cast<int32_t>(ceil_div(layers[l].d_in, BK));
+          L.block0 = blocks;
+          blocks += L.m_tiles * L.n_tiles;
+        }
+        a.n_blocks = blocks;
+      }
+    }
     // 32-bit tile offsets: 128 rows of A or of P (row stride ldp)
     a.off32 = 1;
     for (int l = l0; l < l1; ++l)

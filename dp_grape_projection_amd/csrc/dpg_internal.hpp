@@ -19,6 +19,10 @@ constexpr int kBackN = 64;  // back-projection: 128 x 64 output tiles
 // Partial sums (sum-pass groups, projection splits) are read this many
 // partials at a time, all loads in flight together.
 constexpr int kSumBatch = 8;
+// Large projections (bf16, r and B*T whole multiples of 256, d_in of 64):
+// 256 x 256 output tiles, K steps of 64, operands copied to LDS by direct
+// loads in two stages, 8 waves per block.
+constexpr int kBigM = 256, kBigN = 256, kBigK = 64;
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this
 // many norm partials.
@@ -73,6 +77,7 @@ struct ProjArgs {
   int32_t off32;      // activation tiles addressable with 32-bit byte offsets
   int32_t full;       // every tile and step is full, with off32 and 16-byte rows
   int32_t groups2;    // 8-wave blocks: two wave groups split each block's steps
+  int32_t big;        // proj_big_kernel: kBigM x kBigN tiles, steps of kBigK
 };
 
 struct XsumLayer {

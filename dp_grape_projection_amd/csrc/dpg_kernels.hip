@@ -261,6 +261,142 @@ __device__ __forceinline__ void load_batch(f32x4 (&buf)[kSumBatch], const float*
   }
 }
 
+// Large projections (bf16): a block computes a 256 (rows j of P) x 256
+// (rows n of A) tile of X^T over its K range in steps of 64. Each step's two
+// operand tiles (256 rows x 128 bytes each) are copied into LDS by direct
+// global-to-LDS loads, one step ahead of the matrix cores (two stages). A
+// row's eight 16-byte chunks are stored XOR-swizzled by a function of the row
+// so that the 32 rows an MFMA operand read touches spread over the banks.
+// Waves are 2 (j) x 4 (n); each computes 128 x 64 with 32x32x16 MFMAs, its B
+// operand rows read in the order that gives every lane two consecutive n.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+// vmcnt(0) with the other counters left alone.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Chunk slot of 16-byte chunk c in row R: P tiles by R, A tiles by R / 2
+// (the B operand reads every other row).
+__device__ __forceinline__ int big_slot_p(int R, int c) { return c ^ (R & 7); }
+__device__ __forceinline__ int big_slot_a(int R, int c) { return c ^ ((R >> 1) & 7); }
+
+__global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArgs a) {
+  constexpr int kRowBytes = kBigK * 2;                  // 128
+  constexpr int kTileBytes = kBigM * kRowBytes;         // 32 KiB per operand
+  constexpr int kStageBytes = 2 * kTileBytes;
+  static_assert(kBigM == kBigN && kRowBytes == 128, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  const int lb = xcd_logical_block();
+  if (lb >= a.n_blocks) return;
+  const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const int local = lb - L.block0;
+  const int mt = local % L.m_tiles;
+  const int rest = local / L.m_tiles;
+  const int nt = rest % L.n_tiles;
+  const int split = rest / L.n_tiles;
+  const int j0 = mt * kBigM, n0 = nt * kBigN;
+  const int BT = a.B * a.T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int n_steps_all = L.d_in / kBigK;
+  const int s_begin = split * L.steps_per_split;
+  const int s_end = min(n_steps_all, s_begin + L.steps_per_split);
+  const int n_steps = s_end - s_begin;
+  const char* Pb = static_cast<const char*>(L.P) + static_cast<int64_t>(j0) * L.ldp * 2;
+  const char* Ab = static_cast<const char*>(L.A) + static_cast<int64_t>(n0) * L.d_in * 2;
+  const int64_t p_row = static_cast<int64_t>(L.ldp) * 2, a_row = static_cast<int64_t>(L.d_in) * 2;
+
+  // Copies K step `step` into stage `stage`: 64 instructions of 1 KiB (8 rows)
+  // per step, 8 per wave; instruction q of wave w fills row block q * 8 + w
+  // (blocks 0..31: P, 32..63: A). Lane l writes slot l % 8 of row l / 8.
+  auto issue = [&](int step, int stage) {
+    char* sb = smem + stage * kStageBytes;
+    const int64_t kb = static_cast<int64_t>(s_begin + step) * kRowBytes;
+    const int rl = lane >> 3, slot = lane & 7;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int g = q * 8 + wave;
+      const bool is_a = g >= 32;
+      const int R = (g & 31) * 8 + rl;
+      const int c = is_a ? big_slot_a(R, slot) : big_slot_p(R, slot);  // involution
+      const char* src = (is_a ? Ab + R * a_row : Pb + R * p_row) + kb + c * 16;
+      char* dst = sb + (is_a ? kTileBytes : 0) + (g & 31) * 1024;
+      // (C casts: they are the address-space conversions)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+    }
+  };
+
+  Acc<4, 2> acc;
+  acc.zero();
+  const int r32 = lane & 31, kh = lane >> 5;
+  if (n_steps > 0) issue(0, 0);
+  for (int s = 0; s < n_steps; ++s) {
+    wait_vm0();     // this wave's copies of step s have landed
+    lds_barrier();  // every wave's have, and step s - 1's reads are done
+    if (s + 1 < n_steps) issue(s + 1, (s + 1) & 1);
+    const char* sP = smem + (s & 1) * kStageBytes;
+    const char* sA = sP + kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBigK / 16; ++kk) {
+      const int c = 2 * kk + kh;  // this lane's 16-byte chunk: k = 16 kk + 8 kh
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int j = 128 * wm + 32 * mb + r32;
+        af[mb] = *reinterpret_cast<const bf16x8*>(sP + j * kRowBytes + big_slot_p(j, c) * 16);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int n = 64 * wn + 2 * r32 + nb;
+        bfr[nb] = *reinterpret_cast<const bf16x8*>(sA + n * kRowBytes + big_slot_a(n, c) * 16);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb],
+                                                                 acc.v[mb][nb], 0, 0, 0);
+    }
+  }
+
+  // lane: columns n, n + 1; registers i: rows 8 (i / 4) + 4 kh + i % 4
+  const int n = n0 + 64 * wn + 2 * r32;
+  if (L.splits == 1) {
+    bf16* Xt = static_cast<bf16*>(L.Xt);
+    const int bi = n / a.T, t = n - bi * a.T;
+    const bool pair = t + 1 < a.T;  // n + 1 in the same sample
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = j0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * kh + (i & 3);
+        bf16* dst = Xt + (static_cast<int64_t>(bi) * a.r + j) * a.ldt + t;
+        if (pair && (t & 1) == 0) {
+          const bf16 v2[2] = {from_float<bf16>(acc.v[mb][0][i]), from_float<bf16>(acc.v[mb][1][i])};
+          *reinterpret_cast<uint32_t*>(dst) = __builtin_bit_cast(uint32_t, v2);
+        } else {
+          dst[0] = from_float<bf16>(acc.v[mb][0][i]);
+          const int t1 = pair ? t + 1 : 0, b1 = pair ? bi : bi + 1;
+          Xt[(static_cast<int64_t>(b1) * a.r + j) * a.ldt + t1] = from_float<bf16>(acc.v[mb][1][i]);
+        }
+      }
+  } else {
+    float* part = L.part + static_cast<int64_t>(split) * a.r * BT;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = j0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * kh + (i & 3);
+        *reinterpret_cast<f32x2*>(part + static_cast<int64_t>(j) * BT + n) =
+            f32x2{acc.v[mb][0][i], acc.v[mb][1][i]};
+      }
+  }
+}
+
 // Xt[b][j][t] = sum over splits of part[s][j][b*T + t]; one thread per 4
 // consecutive n of one row j.
 template <typename T>
@@ -961,6 +1097,10 @@ static hipError_t launch_proj_ng(const ProjArgs& a, bool bf16_in, bool vec, hipS
 }
 
 hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
+  if (a.big) {
+    hipLaunchKernelGGL(proj_big_kernel, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   return a.groups2 ? launch_proj_ng<2>(a, bf16_in, vec, s)
                    : launch_proj_ng<1>(a, bf16_in, vec, s);
 }

@@ -109,6 +109,15 @@ CASES = {
     "groups_fp32": W.custom_workload("groups_fp32", 20,
                                      [(32, 6400), (32, 6400)], B=33, T=8,
                                      r=16, dtype="fp32"),
+    # the large-projection kernel (r and B*T multiples of 256, d_in of 64):
+    # unsplit; split over d_in (partials and xsum); odd T (sample boundaries
+    # between a lane's two columns)
+    "big_bf16": W.custom_workload("big_bf16", 25, [(192, 160), (128, 96)], B=2,
+                                  T=256, r=256),
+    "big_split_bf16": W.custom_workload("big_split_bf16", 26, [(2048, 64)], B=2,
+                                        T=256, r=256),
+    "big_odd_t_bf16": W.custom_workload("big_odd_t_bf16", 27, [(64, 32)], B=256,
+                                        T=3, r=256),
     # fewer tiles: sum groups of 2 samples (accumulator rescaled between
     # them), with a single-sample last group
     "groups4_bf16": W.custom_workload("groups4_bf16", 22,
