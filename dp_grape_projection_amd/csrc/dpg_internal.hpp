@@ -22,7 +22,13 @@ constexpr int kSumBatch = 8;
 // Large projections (bf16, r and B*T whole multiples of 256, d_in of 64):
 // 256 x 256 output tiles, K steps of 64, operands copied to LDS by direct
 // loads in two stages, 8 waves per block.
-constexpr int kBigM = 256, kBigN = 256, kBigK = 64;
+#ifndef DPG_BIG_K
+#define DPG_BIG_K 64
+#endif
+#ifndef DPG_BIG_STAGES
+#define DPG_BIG_STAGES 2
+#endif
+constexpr int kBigM = 256, kBigN = 256, kBigK = DPG_BIG_K, kBigStages = DPG_BIG_STAGES;
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this
 // many norm partials.

@@ -272,24 +272,37 @@ __device__ __forceinline__ void load_batch(f32x4 (&buf)[kSumBatch], const float*
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
-// vmcnt(0) with the other counters left alone.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// vmcnt(n) (n < 64) with the other counters left alone.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {  // the encoding must be an immediate
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // (stricter: wait for all)
+  }
+}
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// Chunk slot of 16-byte chunk c in row R: P tiles by R, A tiles by R / 2
-// (the B operand reads every other row).
-__device__ __forceinline__ int big_slot_p(int R, int c) { return c ^ (R & 7); }
-__device__ __forceinline__ int big_slot_a(int R, int c) { return c ^ ((R >> 1) & 7); }
 
+// BK: K step (elements); S: pipeline stages. Rows of a stage are BK * 2 bytes
+// in CH chunks of 16 bytes; chunk c of row R sits in slot c ^ f(R) with
+// f(R) = R (P tiles) or R / 2 (A tiles), modulo CH.
+template <int BK, int S>
 __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArgs a) {
-  constexpr int kRowBytes = kBigK * 2;                  // 128
-  constexpr int kTileBytes = kBigM * kRowBytes;         // 32 KiB per operand
+  constexpr int kRowBytes = BK * 2;
+  constexpr int CH = kRowBytes / 16;                 // chunks per row
+  constexpr int kRowsPerCopy = 1024 / kRowBytes;      // rows per 1 KiB copy
+  constexpr int kCopiesPerTile = kBigM / kRowsPerCopy;
+  constexpr int kCopiesPerWave = 2 * kCopiesPerTile / 8;  // per step
+  constexpr int kTileBytes = kBigM * kRowBytes;
   constexpr int kStageBytes = 2 * kTileBytes;
-  static_assert(kBigM == kBigN && kRowBytes == 128, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  static_assert(kBigM == kBigN && BK % 16 == 0 && (CH & (CH - 1)) == 0, "tile shape");
+  static_assert(kCopiesPerWave * 8 == 2 * kCopiesPerTile, "copies per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[S * kStageBytes];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
@@ -302,29 +315,32 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   const int BT = a.B * a.T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int n_steps_all = L.d_in / kBigK;
+  const int n_steps_all = L.d_in / BK;
   const int s_begin = split * L.steps_per_split;
   const int s_end = min(n_steps_all, s_begin + L.steps_per_split);
   const int n_steps = s_end - s_begin;
   const char* Pb = static_cast<const char*>(L.P) + static_cast<int64_t>(j0) * L.ldp * 2;
   const char* Ab = static_cast<const char*>(L.A) + static_cast<int64_t>(n0) * L.d_in * 2;
   const int64_t p_row = static_cast<int64_t>(L.ldp) * 2, a_row = static_cast<int64_t>(L.d_in) * 2;
+  auto slot_p = [](int R, int c) { return c ^ (R & (CH - 1)); };
+  auto slot_a = [](int R, int c) { return c ^ ((R >> 1) & (CH - 1)); };
 
-  // Copies K step `step` into stage `stage`: 64 instructions of 1 KiB (8 rows)
-  // per step, 8 per wave; instruction q of wave w fills row block q * 8 + w
-  // (blocks 0..31: P, 32..63: A). Lane l writes slot l % 8 of row l / 8.
+  // Copies K step `step` into stage `stage`: copy q of wave w fills row
+  // block g = q * 8 + w (P blocks first, then A blocks); lane l writes slot
+  // l % CH of row l / CH of the block.
   auto issue = [&](int step, int stage) {
     char* sb = smem + stage * kStageBytes;
     const int64_t kb = static_cast<int64_t>(s_begin + step) * kRowBytes;
-    const int rl = lane >> 3, slot = lane & 7;
+    const int rl = lane / CH, slot = lane % CH;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kCopiesPerWave; ++q) {
       const int g = q * 8 + wave;
-      const bool is_a = g >= 32;
-      const int R = (g & 31) * 8 + rl;
-      const int c = is_a ? big_slot_a(R, slot) : big_slot_p(R, slot);  // involution
+      const bool is_a = g >= kCopiesPerTile;
+      const int gi = is_a ? g - kCopiesPerTile : g;
+      const int R = gi * kRowsPerCopy + rl;
+      const int c = is_a ? slot_a(R, slot) : slot_p(R, slot);  // the swizzle is an involution
       const char* src = (is_a ? Ab + R * a_row : Pb + R * p_row) + kb + c * 16;
-      char* dst = sb + (is_a ? kTileBytes : 0) + (g & 31) * 1024;
+      char* dst = sb + (is_a ? kTileBytes : 0) + gi * 1024;
       // (C casts: they are the address-space conversions)
       __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
     }
@@ -333,26 +349,29 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   Acc<4, 2> acc;
   acc.zero();
   const int r32 = lane & 31, kh = lane >> 5;
-  if (n_steps > 0) issue(0, 0);
+#pragma unroll
+  for (int q = 0; q < S - 1; ++q)
+    if (q < n_steps) issue(q, q);
   for (int s = 0; s < n_steps; ++s) {
-    wait_vm0();     // this wave's copies of step s have landed
-    lds_barrier();  // every wave's have, and step s - 1's reads are done
-    if (s + 1 < n_steps) issue(s + 1, (s + 1) & 1);
-    const char* sP = smem + (s & 1) * kStageBytes;
+    // step s has landed when at most the later issued steps are in flight
+    wait_vm(min(S - 2, n_steps - 1 - s) * kCopiesPerWave);
+    lds_barrier();  // every wave's copies of step s landed; step s - 1's reads are done
+    if (s + S - 1 < n_steps) issue(s + S - 1, (s + S - 1) % S);
+    const char* sP = smem + (s % S) * kStageBytes;
     const char* sA = sP + kTileBytes;
 #pragma unroll
-    for (int kk = 0; kk < kBigK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       const int c = 2 * kk + kh;  // this lane's 16-byte chunk: k = 16 kk + 8 kh
       bf16x8 af[4], bfr[2];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const int j = 128 * wm + 32 * mb + r32;
-        af[mb] = *reinterpret_cast<const bf16x8*>(sP + j * kRowBytes + big_slot_p(j, c) * 16);
+        af[mb] = *reinterpret_cast<const bf16x8*>(sP + j * kRowBytes + slot_p(j, c) * 16);
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int n = 64 * wn + 2 * r32 + nb;
-        bfr[nb] = *reinterpret_cast<const bf16x8*>(sA + n * kRowBytes + big_slot_a(n, c) * 16);
+        bfr[nb] = *reinterpret_cast<const bf16x8*>(sA + n * kRowBytes + slot_a(n, c) * 16);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -1098,7 +1117,8 @@ static hipError_t launch_proj_ng(const ProjArgs& a, bool bf16_in, bool vec, hipS
 
 hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
   if (a.big) {
-    hipLaunchKernelGGL(proj_big_kernel, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
+    hipLaunchKernelGGL((proj_big_kernel<kBigK, kBigStages>), dim3(grid8(a.n_blocks)),
+                       dim3(2 * kThreads), 0, s, a);
     return hipGetLastError();
   }
   return a.groups2 ? launch_proj_ng<2>(a, bf16_in, vec, s)
