@@ -149,19 +149,33 @@ constexpr bool kProjBig = DPG_PROJ_BIG != 0;
 
 int step_of(int32_t dtype) { return dtype == DPG_BF16 ? kStepBf16 : kStepF32; }
 
+#ifndef DPG_SAMP_BIG
+#define DPG_SAMP_BIG 1
+#endif
+constexpr bool kSampBig = DPG_SAMP_BIG != 0;
+
+// Tiling of the two per-sample passes (squared-norm partials, clipped sum).
+struct SampPlan {
+  bool big = false;  // samp_big_kernel: kBigM x kBigN tiles, 8 waves
+  std::vector<int32_t> m_tiles, n_tiles, slot0;  // per layer; slot0 in tiles
+  int32_t n_slots = 0;         // partials per sample: one per (tile, wave)
+  int32_t norm_per_block = 1;  // samples per norm block
+  int32_t norm_res_tiles = 0;  // column tiles per norm block (T within one step)
+  int32_t groups = 1, per_group = 1;  // sum pass
+  bool fuse_scale = false;             // sum pass computes s_i itself
+};
+
 struct ProjPlan {
   int64_t ldt = 0;             // row stride of Xt (T rounded up to 8)
   std::vector<int64_t> ldp;    // row stride of P per layer
   std::vector<size_t> off_P, off_Xt, off_part, off_xpart;
-  std::vector<int32_t> m_tiles;  // per-sample passes: 128-row tiles over r
   std::vector<int32_t> m_tiles_proj, n_tiles_proj, splits, steps_per_split;  // projection
-  std::vector<int32_t> n_tiles_s, slot0;  // per-sample passes: tiles over d_out
-  int32_t n_slots = 0;
-  int32_t norm_per_block = 1;  // samples per norm block
   bool big = false;             // projection in proj_big_kernel tiles
-  int32_t norm_res_tiles = 0;  // column tiles per norm block (T within one step)
-  int32_t groups = 1, per_group = 1;  // sum pass
-  bool fuse_scale = false;             // sum pass computes s_i itself
+  // per-sample passes: the regular tiling, and the large one where the
+  // shapes allow it (taken when dY is 16-byte aligned; the workspace holds
+  // either)
+  SampPlan samp, samp_big;
+  bool has_samp_big = false;
   size_t off_norm = 0, off_scales = 0, total = 0;
 };
 
@@ -240,7 +254,6 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     }
   }
   size_t off = 0;
-  int64_t tiles_s = 0;
   for (int l = 0; l < n_layers; ++l) {
     const int64_t ldp = round_up(layers[l].d_in, 8);
     p.ldp.push_back(ldp);
@@ -252,17 +265,25 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     int64_t splits = ceil_div(nsteps, p.big ? big_sps : steps_per_block);
     const int64_t sps = ceil_div(nsteps, splits);
     splits = ceil_div(nsteps, sps);
-    p.m_tiles.push_back(mt);
     p.m_tiles_proj.push_back(p.big ? static_cast<int32_t>(r / kBigM) : mt);
     p.n_tiles_proj.push_back(static_cast<int32_t>(p.big ? BT / kBigN : ceil_div(BT, kTileN)));
     p.splits.push_back(static_cast<int32_t>(splits));
     p.steps_per_split.push_back(static_cast<int32_t>(sps));
     p.off_xpart.push_back(off);
     if (splits > 1) off = align_up(off + static_cast<size_t>(splits) * r * BT * 4);
+  }
+  int64_t d_out_sum = 0;
+  for (int l = 0; l < n_layers; ++l) d_out_sum += layers[l].d_out;
+
+  // Regular per-sample passes: 128 x 128 tiles, 4 waves, two blocks per CU.
+  SampPlan& q = p.samp;
+  int64_t tiles_s = 0;
+  for (int l = 0; l < n_layers; ++l) {
     const int32_t nt = static_cast<int32_t>(ceil_div(layers[l].d_out, kTileN));
-    p.n_tiles_s.push_back(nt);
-    p.slot0.push_back(p.n_slots / 4);
-    p.n_slots += 4 * mt * nt;  // one partial per wave
+    q.m_tiles.push_back(mt);
+    q.n_tiles.push_back(nt);
+    q.slot0.push_back(q.n_slots / 4);
+    q.n_slots += 4 * mt * nt;  // one partial per wave
     tiles_s += static_cast<int64_t>(mt) * nt;
   }
   // Both per-sample passes give each block a run of samples of one tile. The
@@ -281,7 +302,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       const int64_t cost = ceil_div(blocks, target) * per;
       if (best < 0 || cost <= best) {
         best = cost;
-        p.norm_res_tiles = static_cast<int32_t>(per);
+        q.norm_res_tiles = static_cast<int32_t>(per);
       }
     }
   }
@@ -292,7 +313,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       const int64_t cost = ceil_div(tiles_s * ceil_div(B, pb), target) * pb;
       if (best < 0 || cost <= best) {
         best = cost;
-        p.norm_per_block = static_cast<int32_t>(pb);
+        q.norm_per_block = static_cast<int32_t>(pb);
       }
     }
   }
@@ -301,8 +322,6 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // (rounds of resident blocks) x (blocks per round) x (operand bytes per
   // block), plus the partials written and read again (ties: fewer groups).
   {
-    int64_t d_out_sum = 0;
-    for (int l = 0; l < n_layers; ++l) d_out_sum += layers[l].d_out;
     const double tile_bytes =
         static_cast<double>(ceil_div(T, BK)) * BK * (kTileM + kTileN) * es;
     double best = -1.0;
@@ -313,18 +332,73 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       const double part = 2.0 * g * r * static_cast<double>(d_out_sum) * 4.0;
       if (best < 0.0 || main + part < best) {
         best = main + part;
-        p.per_group = static_cast<int32_t>(per);
+        q.per_group = static_cast<int32_t>(per);
       }
     }
   }
-  p.groups = static_cast<int32_t>(ceil_div(B, p.per_group));
-  p.fuse_scale = p.per_group <= kFuseMaxGroup && p.n_slots <= kFuseMaxSlots;
+  q.groups = static_cast<int32_t>(ceil_div(B, q.per_group));
+  q.fuse_scale = q.per_group <= kFuseMaxGroup && q.n_slots <= kFuseMaxSlots;
+
+  // Large per-sample passes (bf16; r, d_out whole 256 x 256 tiles; T whole
+  // K steps): one 8-wave block per CU, launched kMaxLayers layers at a time.
+  // The norm run and the sum group minimise the same estimates, summed over
+  // the launches, with the rounds of resident blocks counted in K steps
+  // (plus two per block for the pipeline's fill).
+  p.has_samp_big = kSampBig && dtype == DPG_BF16 && r % kBigM == 0 && T % kSampBigK == 0;
+  for (int l = 0; l < n_layers; ++l)
+    if (layers[l].d_out % kBigN != 0) p.has_samp_big = false;
+  if (p.has_samp_big) {
+    SampPlan& b = p.samp_big;
+    b.big = true;
+    const int32_t mtb = r / kBigM;
+    std::vector<int64_t> chunk_tiles;
+    for (int l = 0; l < n_layers; ++l) {
+      const int32_t nt = static_cast<int32_t>(layers[l].d_out / kBigN);
+      b.m_tiles.push_back(mtb);
+      b.n_tiles.push_back(nt);
+      b.slot0.push_back(b.n_slots / 8);
+      b.n_slots += 8 * mtb * nt;  // one partial per wave
+      if (l % kMaxLayers == 0) chunk_tiles.push_back(0);
+      chunk_tiles.back() += static_cast<int64_t>(mtb) * nt;
+    }
+    const int64_t cus = target / 2, kc = T / kSampBigK;
+    auto step_rounds = [&](int64_t per) {
+      const int64_t runs = ceil_div(B, per);
+      int64_t t = 0;
+      for (int64_t c : chunk_tiles) t += ceil_div(c * runs, cus) * (per * kc + 2);
+      return t;
+    };
+    int64_t best = -1;
+    for (int64_t pb = 1; pb <= B; ++pb) {
+      const int64_t cost = step_rounds(pb);
+      if (best < 0 || cost <= best) {
+        best = cost;
+        b.norm_per_block = static_cast<int32_t>(pb);
+      }
+    }
+    const double step_bytes = static_cast<double>(kBigM + kBigN) * kSampBigK * es;
+    double best_sum = -1.0;
+    for (int64_t per = std::min<int64_t>(B, kSumMaxGroup); per >= 1; --per) {
+      const int64_t g = ceil_div(B, per);
+      const double cost = static_cast<double>(step_rounds(per)) * cus * step_bytes +
+                          2.0 * g * r * static_cast<double>(d_out_sum) * 4.0;
+      if (best_sum < 0.0 || cost < best_sum) {
+        best_sum = cost;
+        b.per_group = static_cast<int32_t>(per);
+      }
+    }
+    b.groups = static_cast<int32_t>(ceil_div(B, b.per_group));
+    b.fuse_scale = b.per_group <= kFuseMaxGroup && b.n_slots <= kFuseMaxSlots;
+  }
+
+  const int32_t groups = std::max(q.groups, p.has_samp_big ? p.samp_big.groups : 0);
+  const int32_t n_slots = std::max(q.n_slots, p.has_samp_big ? p.samp_big.n_slots : 0);
   for (int l = 0; l < n_layers; ++l) {
     p.off_part.push_back(off);
-    off = align_up(off + static_cast<size_t>(p.groups) * r * layers[l].d_out * 4);
+    off = align_up(off + static_cast<size_t>(groups) * r * layers[l].d_out * 4);
   }
   p.off_norm = off;
-  off = align_up(off + static_cast<size_t>(B) * p.n_slots * 4);
+  off = align_up(off + static_cast<size_t>(B) * n_slots * 4);
   p.off_scales = off;
   off = align_up(off + static_cast<size_t>(B) * 4);
   p.total = off;
@@ -650,20 +724,28 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     }
   }
 
+  // the large per-sample kernel copies dY rows with 16-byte transfers; the
+  // streaming form (which also stores each sample's product) takes the
+  // regular one
+  bool samp_big = p.has_samp_big && !layer_mode;
+  for (int l = 0; l < n_layers; ++l)
+    if (!aligned(layers[l].dY, 16)) samp_big = false;
+  const SampPlan& sp = samp_big ? p.samp_big : p.samp;
   auto fill_samp = [&](SampArgs& a, int l0, int l1, bool sum, bool* pair) {
     std::memset(&a, 0, sizeof(a));
+    a.big = sp.big;
     a.B = static_cast<int32_t>(B);
     a.T = static_cast<int32_t>(T);
     a.r = r;
     a.ldt = static_cast<int32_t>(p.ldt);
-    a.per_block = sum ? p.per_group : p.norm_per_block;
-    a.res_tiles = sum ? 0 : p.norm_res_tiles;
-    a.n_slots = p.n_slots;
+    a.per_block = sum ? sp.per_group : sp.norm_per_block;
+    a.res_tiles = sum ? 0 : sp.norm_res_tiles;
+    a.n_slots = sp.n_slots;
     a.norm_part = norm_part;
     a.scales = scales;
-    a.fuse_scale = sum && p.fuse_scale;
+    a.fuse_scale = sum && sp.fuse_scale;
     a.clip_C = static_cast<float>(clip_C);
-    a.norms_out = (sum && p.fuse_scale && l0 == 0) ? sample_norms : nullptr;
+    a.norms_out = (sum && sp.fuse_scale && l0 == 0) ? sample_norms : nullptr;
     const int64_t runs = ceil_div(B, a.per_block);
     int blocks = 0;
     *pair = true;
@@ -673,9 +755,9 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       L.Xt = ws + p.off_Xt[l];
       L.part = reinterpret_cast<float*>(ws + p.off_part[l]);
       L.d_out = static_cast<int32_t>(layers[l].d_out);
-      L.m_tiles = p.m_tiles[l];
-      L.n_tiles = p.n_tiles_s[l];
-      L.slot0 = p.slot0[l];
+      L.m_tiles = sp.m_tiles[l];
+      L.n_tiles = sp.n_tiles[l];
+      L.slot0 = sp.slot0[l];
       L.block0 = blocks;
       if (a.res_tiles > 0) {
         L.n_chunks = static_cast<int32_t>(ceil_div(L.n_tiles, a.res_tiles));
@@ -709,15 +791,15 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       return st;
   }
   if (layer_mode) {
-    NormAccArgs a{norm_part, p.n_slots, static_cast<int32_t>(B), norm_sq};
+    NormAccArgs a{norm_part, sp.n_slots, static_cast<int32_t>(B), norm_sq};
     return timed(K_CLIP, s, [&] { return launch_norm_acc(a, s); });
   }
   // 4. per-sample norm and clip factor (needs every layer's partials); the
   //    sum pass does it itself when the groups are small
-  if (!p.fuse_scale) {
+  if (!sp.fuse_scale) {
     ScaleArgs a;
     a.norm_part = norm_part;
-    a.n_slots = p.n_slots;
+    a.n_slots = sp.n_slots;
     a.clip_C = static_cast<float>(clip_C);
     a.scales = scales;
     a.norms_out = sample_norms;
@@ -735,7 +817,7 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       return st;
     FinArgs f;
     std::memset(&f, 0, sizeof(f));
-    f.groups = p.groups;
+    f.groups = sp.groups;
     f.noise_scale = static_cast<float>(noise);
     f.inv_B = static_cast<float>(1.0 / static_cast<double>(B));
     f.k0 = k0;

@@ -29,6 +29,7 @@ constexpr int kSumBatch = 8;
 #define DPG_BIG_STAGES 2
 #endif
 constexpr int kBigM = 256, kBigN = 256, kBigK = DPG_BIG_K, kBigStages = DPG_BIG_STAGES;
+constexpr int kSampBigK = 64;  // K step (over t) of the large norm and sum kernel
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this
 // many norm partials.
@@ -132,6 +133,8 @@ struct SampArgs {
   float clip_C;         // sum mode, fused
   float* norms_out;     // sum mode, fused: [B] or null (written by layer 0's
                         // first tile of each group)
+  int32_t big;          // samp_big_kernel: kBigM x kBigN tiles, steps of
+                        // kSampBigK, 8 partial slots per (sample, tile)
 };
 
 // ---- n_i, s_i from the partials

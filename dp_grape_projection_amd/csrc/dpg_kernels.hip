@@ -666,6 +666,194 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
   }
 }
 
+// Norm and sum passes in 256 x 256 tiles (rows j of Xt over r, columns n of
+// dY over d_out) for bf16 with r and d_out whole tiles and T a multiple of
+// kSampBigK: one 8-wave block per CU, K steps over t, two stages of direct
+// global-to-LDS copies, the step index running over (sample, t) so that the
+// copies flow on across the samples of a block. Xt tiles (t contiguous) sit
+// in LDS as the projection's P tiles do. dY tiles stay row-major [t][n], 512
+// bytes a row, chunk c of row t in slot c ^ 4 (t % 4); the matrix cores' B
+// operand is read from them with the transposing LDS read: in each group of
+// 16 lanes, lane q gives four consecutive n of row t0 + q / 4, and lane j
+// receives element j % 4 of what lanes j / 4, 4 + j / 4, 8 + j / 4 and
+// 12 + j / 4 gave, i.e. four consecutive t of one column. Waves are 2 (j) x 4
+// (n), each computing 128 x 64. Norm mode writes one squared-norm partial per
+// (sample, tile, wave); sum mode keeps the running clipped sum of samp_kernel.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <bool SUM>
+__global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArgs a) {
+  constexpr int BK = kSampBigK;
+  constexpr int kRowA = BK * 2, CHA = kRowA / 16;        // Xt tile rows
+  constexpr int kRowB = kBigN * 2, CHB = kRowB / 16;     // dY tile rows
+  constexpr int kTileBytes = kBigM * kRowA;
+  constexpr int kBlocksA = kTileBytes / 1024;            // 1 KiB copies per tile
+  constexpr int kCopies = 2 * kBlocksA / 8;              // per wave and step
+  constexpr int kStageBytes = 2 * kTileBytes;
+  static_assert(kTileBytes == BK * kRowB && kBigM == kBigN, "equal square tiles");
+  static_assert(kCopies * 8 == 2 * kBlocksA && kCopies % 2 == 0, "copies per wave");
+  static_assert(CHA == 8 && CHB == 32, "swizzles assume 128- and 512-byte rows");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  __shared__ float s_grp[SUM ? kSumMaxGroup : 1];
+  const int lb = xcd_logical_block();
+  if (lb >= a.n_blocks) return;
+  const int li = find_layer(a.L, a.n_layers, lb);
+  const SampLayer& L = a.L[li];
+  const int local = lb - L.block0;
+  const int mt = local % L.m_tiles;
+  const int rest = local / L.m_tiles;
+  const int nt = rest % L.n_tiles;
+  const int g = rest / L.n_tiles;  // run (norm) or group (sum) of samples
+  const int j0 = mt * kBigM, n0 = nt * kBigN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int i_begin = g * a.per_block;
+  const int i_end = min(a.B, i_begin + a.per_block);
+  const int kc = a.T / BK;  // steps per sample
+  const int n_steps = (i_end - i_begin) * kc;
+  const char* Xt = static_cast<const char*>(L.Xt);
+  const char* dY = static_cast<const char*>(L.dY);
+  const int64_t x_row = static_cast<int64_t>(a.ldt) * 2, y_row = static_cast<int64_t>(L.d_out) * 2;
+  auto slot_a = [](int R, int c) { return c ^ (R & (CHA - 1)); };
+  auto slot_b = [](int R, int c) { return c ^ (4 * (R & 3)); };
+
+  // Copies step `step` into stage `stage`: copy q of wave w fills 1 KiB
+  // block q * 8 + w (Xt blocks of 8 rows first, then dY blocks of 2 rows);
+  // lane l writes the block's 16-byte slot l.
+  auto issue = [&](int step, int stage) {
+    char* sb = smem + stage * kStageBytes;
+    const int i = i_begin + step / kc, k0 = (step % kc) * BK;
+    const char* Xb = Xt + (static_cast<int64_t>(i) * a.r + j0) * x_row + k0 * 2;
+    const char* Yb = dY + (static_cast<int64_t>(i) * a.T + k0) * y_row + n0 * 2;
+#pragma unroll
+    for (int q = 0; q < kCopies; ++q) {
+      const int blk = q * 8 + wave;
+      const char* src;
+      if (q < kCopies / 2) {
+        const int R = blk * (1024 / kRowA) + lane / CHA;
+        src = Xb + R * x_row + slot_a(R, lane % CHA) * 16;  // the swizzles are involutions
+      } else {
+        const int R = (blk - kBlocksA) * (1024 / kRowB) + lane / CHB;
+        src = Yb + R * y_row + slot_b(R, lane % CHB) * 16;
+      }
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(sb + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  if (SUM) {
+    if (!a.fuse_scale) {
+      for (int q = tid; q < i_end - i_begin; q += 2 * kThreads) s_grp[q] = a.scales[i_begin + q];
+    } else {
+      // per-sample global norm and clip factor of this group, summed in the
+      // same order as samp_kernel (wave w takes samples w, w + 8, ...)
+      const int jn = (a.n_slots + 63) >> 6;
+      for (int q = wave; q < i_end - i_begin; q += 8) {
+        const float* p = a.norm_part + static_cast<int64_t>(i_begin + q) * a.n_slots;
+        float v[kFuseMaxSlots / 64];
+#pragma unroll
+        for (int j = 0; j < kFuseMaxSlots / 64; ++j)
+          if (j < jn) v[j] = p[min(lane + 64 * j, a.n_slots - 1)];
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kFuseMaxSlots / 64; ++j)
+          if (j < jn && lane + 64 * j < a.n_slots) t += v[j];
+        const float n = sqrtf(wave_sum(t));
+        if (lane == 0) {
+          s_grp[q] = (n > a.clip_C) ? a.clip_C / n : 1.0f;
+          if (a.norms_out && li == 0 && mt == 0 && nt == 0) a.norms_out[i_begin + q] = n;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  Acc<4, 2> acc;
+  acc.zero();
+  float c = 0.0f;  // sum mode: factor the accumulator is expressed in
+  bool on = true;  // sum mode: the current sample is accumulated
+  const int r32 = lane & 31, kh = lane >> 5;
+  const int q16 = lane & 15, nh = (lane >> 4) & 1;
+  if (n_steps > 0) issue(0, 0);
+  for (int s = 0; s < n_steps; ++s) {
+    wait_vm(0);
+    lds_barrier();  // step s landed for every wave; step s - 1's reads are done
+    const char* sX = smem + (s & 1) * kStageBytes;
+    const char* sY = sX + kTileBytes;
+    // The B fragments of the whole step are read before the next step's
+    // copies are issued: the compiler makes transposing LDS reads wait for
+    // every copy in flight.
+    bf16x8 bfr[BK / 16][2];
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // rows t = 16 kk + 8 kh + 4 h + q16 / 4, columns n .. n + 3
+        const int n = 64 * wn + 32 * nb + 16 * nh + 4 * (q16 & 3);
+        v4i16 h2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = 16 * kk + 8 * kh + 4 * h + (q16 >> 2);
+          const char* p = sY + t * kRowB + slot_b(t, n >> 3) * 16 + (n & 7) * 2;
+          h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+        }
+        bfr[kk][nb] = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    if (s + 1 < n_steps) issue(s + 1, (s + 1) & 1);
+    if (SUM && s % kc == 0) {
+      const float si = s_grp[s / kc];
+      on = si > 0.0f;
+      if (on) {
+        if (c != 0.0f && c != si) acc.scale(c / si);
+        c = si;
+      }
+    }
+    if (on) {
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cx = 2 * kk + kh;  // this lane's Xt chunk: t = 16 kk + 8 kh ..
+        bf16x8 af[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int j = 128 * wm + 32 * mb + r32;
+          af[mb] = *reinterpret_cast<const bf16x8*>(sX + j * kRowA + slot_a(j, cx) * 16);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[kk][nb],
+                                                                   acc.v[mb][nb], 0, 0, 0);
+      }
+    }
+    if (!SUM && s % kc == kc - 1) {
+      const int i = i_begin + s / kc;
+      const float t = wave_sum(acc.sum_sq());
+      if (lane == 0)
+        a.norm_part[static_cast<int64_t>(i) * a.n_slots +
+                    8 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+      acc.zero();
+    }
+  }
+
+  if (SUM) {
+    // lane: column n0 + 64 wn + 32 nb + r32; registers i: rows
+    // 8 (i / 4) + 4 kh + i % 4 of its 32-row block
+    acc.scale(c);
+    float* part = L.part + static_cast<int64_t>(g) * a.r * L.d_out;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = j0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * kh + (i & 3);
+          part[static_cast<int64_t>(j) * L.d_out + n0 + 64 * wn + 32 * nb + r32] = acc.v[mb][nb][i];
+        }
+  }
+}
+
 // ------------------------------------------------------------------ scale --
 
 __global__ __launch_bounds__(kThreads) void scale_kernel(const ScaleArgs a) {
@@ -1151,6 +1339,10 @@ static hipError_t launch_samp(const SampArgs& a, bool bf16_in, bool pair,
 
 hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
                             hipStream_t s) {
+  if (a.big) {
+    hipLaunchKernelGGL(samp_big_kernel<false>, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.res_tiles == 0) return launch_samp<kTileN, false>(a, bf16_in, pair, s);
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (bf16_in) {
@@ -1166,6 +1358,10 @@ hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
 
 hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
                            hipStream_t s) {
+  if (a.big) {
+    hipLaunchKernelGGL(samp_big_kernel<true>, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   return launch_samp<kTileN, true>(a, bf16_in, pair, s);
 }
 

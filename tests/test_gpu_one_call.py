@@ -53,6 +53,9 @@ CASES = {
                                    B=3, T=8, r=16),
     "groups_bf16": W.custom_workload("o_groups_bf16", 47, [(32, 6400), (32, 6400)],
                                      B=33, T=8, r=16),
+    # the large norm and sum kernel
+    "samp_big_bf16": W.custom_workload("o_samp_big_bf16", 48, [(128, 256), (64, 512)],
+                                       B=3, T=128, r=256),
 }
 
 

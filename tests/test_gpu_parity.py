@@ -118,6 +118,19 @@ CASES = {
                                         T=256, r=256),
     "big_odd_t_bf16": W.custom_workload("big_odd_t_bf16", 27, [(64, 32)], B=256,
                                         T=3, r=256),
+    # the large norm and sum kernel (r and d_out multiples of 256, T of 64):
+    # two layers, several K steps per sample; r of two tiles with one K step
+    # per sample; more than 1024 partials per sample (separate scale
+    # launch); enough tiles that norm runs and sum groups hold 4 samples
+    "samp_big_bf16": W.custom_workload("samp_big_bf16", 28, [(128, 256), (64, 512)],
+                                       B=3, T=128, r=256),
+    "samp_big_r512_bf16": W.custom_workload("samp_big_r512_bf16", 29,
+                                            [(96, 256), (256, 768)], B=5, T=64,
+                                            r=512),
+    "samp_big_wide_bf16": W.custom_workload("samp_big_wide_bf16", 30, [(32, 33024)],
+                                            B=2, T=64, r=256),
+    "samp_big_groups_bf16": W.custom_workload("samp_big_groups_bf16", 31,
+                                              [(32, 10240)], B=16, T=64, r=256),
     # fewer tiles: sum groups of 2 samples (accumulator rescaled between
     # them), with a single-sample last group
     "groups4_bf16": W.custom_workload("groups4_bf16", 22,
