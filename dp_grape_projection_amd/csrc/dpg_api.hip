@@ -149,6 +149,16 @@ constexpr bool kProjBig = DPG_PROJ_BIG != 0;
 
 int step_of(int32_t dtype) { return dtype == DPG_BF16 ? kStepBf16 : kStepF32; }
 
+#ifndef DPG_BACK_BIG
+#define DPG_BACK_BIG 1
+#endif
+constexpr bool kBackBig = DPG_BACK_BIG != 0;
+
+#ifndef DPG_HAT_SUM
+#define DPG_HAT_SUM 1
+#endif
+constexpr bool kHatSum = DPG_HAT_SUM != 0;
+
 #ifndef DPG_SAMP_BIG
 #define DPG_SAMP_BIG 1
 #endif
@@ -176,6 +186,11 @@ struct ProjPlan {
   // either)
   SampPlan samp, samp_big;
   bool has_samp_big = false;
+  // T long against r (8 r <= T): the norm pass also stores every sample's
+  // product [r][d_out] (fp32, in the partial region), and the final pass
+  // sums those with the clip factors as weights instead of a second pass
+  // over dY; the stored products move at most half the bytes of dY
+  bool hat_sum = false;
   size_t off_norm = 0, off_scales = 0, total = 0;
 };
 
@@ -391,7 +406,10 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     b.fuse_scale = b.per_group <= kFuseMaxGroup && b.n_slots <= kFuseMaxSlots;
   }
 
-  const int32_t groups = std::max(q.groups, p.has_samp_big ? p.samp_big.groups : 0);
+  p.hat_sum = kHatSum && 8 * static_cast<int64_t>(r) <= T;
+  const int32_t groups = std::max<int64_t>({static_cast<int64_t>(q.groups),
+                                            p.has_samp_big ? p.samp_big.groups : 0,
+                                            p.hat_sum ? B : 0});
   const int32_t n_slots = std::max(q.n_slots, p.has_samp_big ? p.samp_big.n_slots : 0);
   for (int l = 0; l < n_layers; ++l) {
     p.off_part.push_back(off);
@@ -507,6 +525,50 @@ int enqueue_back(const dpg_layer_param* params, int l0, int l1, int32_t r,
         b.res_tiles = static_cast<int32_t>(per);
       }
     }
+  }
+  // Large bf16 back-projections (r over one step, a multiple of kSampBigK;
+  // d_in and d_out whole 256 x 256 tiles; 16-byte aligned rows): one 8-wave
+  // block per CU sweeps a run of column tiles, the run minimising (rounds of
+  // resident blocks) x (tiles per block) x (K steps per tile plus about four
+  // steps' worth of W traffic), ties to the longer run.
+  b.big = kBackBig && bf16 && r % kSampBigK == 0 && r > step_of(dtype);
+  for (int l = l0; l < l1; ++l)
+    if (params[l].d_in % kBigM != 0 || params[l].d_out % kBigN != 0 ||
+        !aligned(params[l].W, 16) || !aligned(P_of(l), 16) || !aligned(U_of(l), 16) ||
+        (ldp_of(l) * elem_size(dtype)) % 16 != 0)
+      b.big = 0;
+  if (b.big) {
+    int64_t best = -1, max_nt = 1;
+    for (int l = l0; l < l1; ++l) max_nt = std::max<int64_t>(max_nt, params[l].d_out / kBigN);
+    const int64_t cus = target_blocks(dtype) / 2, kr = r / kSampBigK;
+    for (int64_t per = 1; per <= max_nt; ++per) {
+      int64_t nb = 0;
+      for (int l = l0; l < l1; ++l)
+        nb += (params[l].d_in / kBigM) * ceil_div(params[l].d_out / kBigN, per);
+      const int64_t cost = ceil_div(nb, cus) * per * (kr + 4);
+      if (best < 0 || cost <= best) {
+        best = cost;
+        b.res_tiles = static_cast<int32_t>(per);
+      }
+    }
+    int blocks = 0;
+    for (int l = l0; l < l1; ++l) {
+      BackLayer& L = b.L[l - l0];
+      L.P = P_of(l);
+      L.U = U_of(l);
+      L.ldp = static_cast<int32_t>(ldp_of(l));
+      L.W = params[l].W;
+      L.d_in = static_cast<int32_t>(params[l].d_in);
+      L.d_out = static_cast<int32_t>(params[l].d_out);
+      L.m_tiles = static_cast<int32_t>(params[l].d_in / kBigM);
+      L.n_tiles = static_cast<int32_t>(params[l].d_out / kBigN);
+      L.n_chunks = static_cast<int32_t>(ceil_div(L.n_tiles, b.res_tiles));
+      L.block0 = blocks;
+      blocks += L.m_tiles * L.n_chunks;
+    }
+    b.n_layers = l1 - l0;
+    b.n_blocks = blocks;
+    return timed(K_BACK, s, [&] { return launch_back(b, bf16, true, s); });
   }
   int blocks = 0;
   bool pair = true;
@@ -727,6 +789,7 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // the large per-sample kernel copies dY rows with 16-byte transfers; the
   // streaming form (which also stores each sample's product) takes the
   // regular one
+  const bool hat_sum = p.hat_sum && !layer_mode;
   bool samp_big = p.has_samp_big && !layer_mode;
   for (int l = 0; l < n_layers; ++l)
     if (!aligned(layers[l].dY, 16)) samp_big = false;
@@ -780,13 +843,16 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     for (int l = l0; l < l1; ++l)
       if (layers[l].d_out % kTileN != 0) a.full = 0;
   };
-  // 3. squared-norm partials of every (sample, layer, tile)
+  // 3. squared-norm partials of every (sample, layer, tile), and with
+  //    hat_sum every sample's product
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int l1 = std::min(n_layers, l0 + kMaxLayers);
     SampArgs a;
     bool pair;
     fill_samp(a, l0, l1, false, &pair);
     if (layer_mode) a.L[0].ghat = ghat;
+    if (hat_sum)
+      for (int l = l0; l < l1; ++l) a.L[l - l0].ghat = reinterpret_cast<float*>(ws + p.off_part[l]);
     if ((st = timed(K_NORM, s, [&] { return launch_samp_norm(a, bf16, pair, s); })))
       return st;
   }
@@ -796,7 +862,7 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   }
   // 4. per-sample norm and clip factor (needs every layer's partials); the
   //    sum pass does it itself when the groups are small
-  if (!sp.fuse_scale) {
+  if (!sp.fuse_scale || hat_sum) {
     ScaleArgs a;
     a.norm_part = norm_part;
     a.n_slots = sp.n_slots;
@@ -806,18 +872,23 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     if ((st = timed(K_SCALE, s, [&] { return launch_scale(a, static_cast<int>(B), s); })))
       return st;
   }
-  // 5-6. clipped sum over samples, then noise and 1/B
+  // 5-6. clipped sum over samples (or, with hat_sum, over the stored
+  //      products weighted by the clip factors in the final pass), then
+  //      noise and 1/B
   const double noise = sigma == 0.0 ? 0.0 : sigma * clip_C;
   for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
     const int l1 = std::min(n_layers, l0 + kMaxLayers);
     SampArgs a;
     bool pair;
-    fill_samp(a, l0, l1, true, &pair);
-    if ((st = timed(K_SUM, s, [&] { return launch_samp_sum(a, bf16, pair, s); })))
-      return st;
+    if (!hat_sum) {
+      fill_samp(a, l0, l1, true, &pair);
+      if ((st = timed(K_SUM, s, [&] { return launch_samp_sum(a, bf16, pair, s); })))
+        return st;
+    }
     FinArgs f;
     std::memset(&f, 0, sizeof(f));
-    f.groups = sp.groups;
+    f.groups = hat_sum ? static_cast<int32_t>(B) : sp.groups;
+    f.weights = hat_sum ? scales : nullptr;
     f.noise_scale = static_cast<float>(noise);
     f.inv_B = static_cast<float>(1.0 / static_cast<double>(B));
     f.k0 = k0;

@@ -229,7 +229,9 @@ struct BackArgs {
   int32_t full;       // every tile and step full (d_in, d_out whole tiles, r
                       // whole steps), with off32 and paired columns
   int32_t res_tiles;  // r within one step: a block keeps its P tile in LDS
-                      // and sweeps this many column tiles (0: one tile)
+                      // and sweeps this many column tiles (0: one tile); with
+                      // big, the run of column tiles of a block
+  int32_t big;        // back_big_kernel: kBigM x kBigN tiles, steps of kSampBigK
 };
 
 // Launchers (dpg_kernels.hip). Each returns the hipError_t of its launch.

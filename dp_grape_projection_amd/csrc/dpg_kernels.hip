@@ -682,6 +682,35 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// Slot of 16-byte chunk c in row k of a k-major LDS tile with 512-byte rows.
+__device__ __forceinline__ int kmajor_slot(int k, int c) { return c ^ (4 * (k & 3)); }
+
+// Transposing LDS read of four 16-bit values. The restrict-qualified pointer
+// gives the read alias-scope information; without it the compiler makes the
+// read wait for every direct global-to-LDS copy in flight (the kernels order
+// those copies against their reads with explicit waits and barriers).
+__device__ __forceinline__ v4i16 lds_read_tr(const char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+}
+
+// Matrix-core operand of a 32x32x16 product from a k-major LDS tile (rows of
+// 512 bytes, kmajor_slot swizzle): lane l receives rows k0 + 8 (l / 32) ..
+// + 7 of column c0 + l % 32. In each group of 16 lanes, lane q addresses four
+// consecutive columns of row k0 + 8 (l / 32) + 4 h + q / 4; the transposing
+// read hands lane j element j % 4 of the values lanes j / 4, 4 + j / 4, ...
+// addressed, which is four consecutive rows of one column.
+__device__ __forceinline__ bf16x8 frag_kmajor(const char* tile, int k0, int c0, int lane) {
+  const int q16 = lane & 15, nh = (lane >> 4) & 1, kh = lane >> 5;
+  const int n = c0 + 16 * nh + 4 * (q16 & 3);
+  v4i16 h[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = k0 + 8 * kh + 4 * i + (q16 >> 2);
+    h[i] = lds_read_tr(tile + t * 512 + kmajor_slot(t, n >> 3) * 16 + (n & 7) * 2);
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <bool SUM>
 __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArgs a) {
   constexpr int BK = kSampBigK;
@@ -716,7 +745,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   const char* dY = static_cast<const char*>(L.dY);
   const int64_t x_row = static_cast<int64_t>(a.ldt) * 2, y_row = static_cast<int64_t>(L.d_out) * 2;
   auto slot_a = [](int R, int c) { return c ^ (R & (CHA - 1)); };
-  auto slot_b = [](int R, int c) { return c ^ (4 * (R & 3)); };
 
   // Copies step `step` into stage `stage`: copy q of wave w fills 1 KiB
   // block q * 8 + w (Xt blocks of 8 rows first, then dY blocks of 2 rows);
@@ -735,7 +763,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
         src = Xb + R * x_row + slot_a(R, lane % CHA) * 16;  // the swizzles are involutions
       } else {
         const int R = (blk - kBlocksA) * (1024 / kRowB) + lane / CHB;
-        src = Yb + R * y_row + slot_b(R, lane % CHB) * 16;
+        src = Yb + R * y_row + kmajor_slot(R, lane % CHB) * 16;
       }
       __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(sb + blk * 1024), 16, 0, 0);
     }
@@ -773,33 +801,19 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   float c = 0.0f;  // sum mode: factor the accumulator is expressed in
   bool on = true;  // sum mode: the current sample is accumulated
   const int r32 = lane & 31, kh = lane >> 5;
-  const int q16 = lane & 15, nh = (lane >> 4) & 1;
   if (n_steps > 0) issue(0, 0);
   for (int s = 0; s < n_steps; ++s) {
     wait_vm(0);
     lds_barrier();  // step s landed for every wave; step s - 1's reads are done
     const char* sX = smem + (s & 1) * kStageBytes;
     const char* sY = sX + kTileBytes;
-    // The B fragments of the whole step are read before the next step's
-    // copies are issued: the compiler makes transposing LDS reads wait for
-    // every copy in flight.
+    // the B fragments of the whole step, read before the next step's copies
+    // are issued
     bf16x8 bfr[BK / 16][2];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        // rows t = 16 kk + 8 kh + 4 h + q16 / 4, columns n .. n + 3
-        const int n = 64 * wn + 32 * nb + 16 * nh + 4 * (q16 & 3);
-        v4i16 h2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int t = 16 * kk + 8 * kh + 4 * h + (q16 >> 2);
-          const char* p = sY + t * kRowB + slot_b(t, n >> 3) * 16 + (n & 7) * 2;
-          h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-        }
-        bfr[kk][nb] = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+      for (int nb = 0; nb < 2; ++nb) bfr[kk][nb] = frag_kmajor(sY, 16 * kk, 64 * wn + 32 * nb, lane);
     if (s + 1 < n_steps) issue(s + 1, (s + 1) & 1);
     if (SUM && s % kc == 0) {
       const float si = s_grp[s / kc];
@@ -833,6 +847,31 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
       if (lane == 0)
         a.norm_part[static_cast<int64_t>(i) * a.n_slots +
                     8 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+      if (L.ghat) {
+        // the sample's product tile into ghat [B][r][d_out], through a buffer
+        // resource on the wave's 128 rows (lane: column n0 + 64 wn + 32 nb +
+        // r32; register q: row 32 mb + 8 (q / 4) + 4 kh + q % 4)
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(
+            L.ghat + (static_cast<int64_t>(i) * a.r + j0 + 128 * wm) * L.d_out);
+        const uint32_t row4 = static_cast<uint32_t>(L.d_out) * 4u;
+        const uint32_t lo = static_cast<uint32_t>(4 * kh) * row4 +
+                            static_cast<uint32_t>(n0 + 64 * wn + r32) * 4u;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              // (the element is copied out first: a bit cast of a vector
+              // element lvalue compiles to a cast of element 0)
+              const float x = acc.v[mb][nb][q];
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __builtin_bit_cast(uint32_t, x), rs, lo + 128u * nb,
+                  __builtin_amdgcn_readfirstlane(
+                      static_cast<uint32_t>(32 * mb + 8 * (q >> 2) + (q & 3)) * row4),
+                  0);
+            }
+      }
       acc.zero();
     }
   }
@@ -910,10 +949,13 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
       const StreamKey key{a.k0, a.k1, a.step_word, 1u};
       normals_at(key, L.layer_id, static_cast<uint32_t>(c), z);
     }
+    // with weights, a sample whose factor is 0 (its norm overflowed) is
+    // skipped rather than multiplied
     f32x4 s = buf[0];
     if (a.weights) {
+      const float w = a.weights[0];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s[q] *= a.weights[0];
+      for (int q = 0; q < 4; ++q) s[q] = w != 0.0f ? s[q] * w : 0.0f;
     }
     for (int g0 = 0; g0 < a.groups; g0 += kSumBatch) {
       if (g0 > 0) load_batch(buf, part + g0 * plane, plane, a.groups - g0);
@@ -924,8 +966,10 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
         if (g > last) break;
         if (a.weights) {
           const float w = a.weights[g];
+          if (w != 0.0f) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) s[q] = fmaf(w, buf[j][q], s[q]);
+            for (int q = 0; q < 4; ++q) s[q] = fmaf(w, buf[j][q], s[q]);
+          }
         } else {
           s[0] += buf[j][0];
           s[1] += buf[j][1];
@@ -964,7 +1008,8 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
       float s = 0.0f;
       for (int g = 0; g < a.groups; ++g) {
         const float v = L.part[g * static_cast<int64_t>(L.n_elem) + e];
-        s = a.weights ? fmaf(a.weights[g], v, s) : s + v;
+        if (!a.weights) s += v;
+        else if (a.weights[g] != 0.0f) s = fmaf(a.weights[g], v, s);
       }
       const float o = fmaf(a.noise_scale, z[q], s) * a.inv_B;
       L.out[e] = o;
@@ -1224,6 +1269,136 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
   }
 }
 
+// W -= lr P^T U in 256 x 256 tiles (rows m of W over d_in, columns n over
+// d_out) for bf16 with d_in, d_out whole tiles and r a multiple of kSampBigK:
+// one 8-wave block per CU sweeps a run of column tiles of one row tile, its K
+// steps over r running on from tile to tile, with two stages of direct
+// global-to-LDS copies. P [r][d_in] and U [r][d_out] are k-major and stay so
+// in LDS (512-byte rows); both matrix-core operands come from the
+// transposing LDS read. A tile's W update runs while the copies of the next
+// tile's first step are in flight; half of its W is fetched before the
+// tile's last step. Waves are 2 (m) x 4 (n), each 128 x 64.
+__global__ __launch_bounds__(2 * kThreads, 1) void back_big_kernel(const BackArgs a) {
+  constexpr int BK = kSampBigK;
+  constexpr int kRow = kBigN * 2;                       // 512-byte rows
+  constexpr int kTileBytes = BK * kRow;
+  constexpr int kBlocks = kTileBytes / 1024;            // 1 KiB copies per tile
+  constexpr int kCopies = 2 * kBlocks / 8;              // per wave and step
+  constexpr int kStageBytes = 2 * kTileBytes;
+  static_assert(kBigM == kBigN && kRow == 512, "k-major tiles of 512-byte rows");
+  static_assert(kCopies * 8 == 2 * kBlocks && kCopies % 2 == 0, "copies per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  const int lb = xcd_logical_block();
+  if (lb >= a.n_blocks) return;
+  const BackLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const int local = lb - L.block0;
+  const int mt = local % L.m_tiles, ch = local / L.m_tiles;
+  const int nt0 = ch * a.res_tiles, nt1 = min(L.n_tiles, nt0 + a.res_tiles);
+  const int m0 = mt * kBigM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r32 = lane & 31, kh = lane >> 5;
+  const int kr = a.r / BK;  // steps per tile
+  const int n_steps = (nt1 - nt0) * kr;
+  const char* P = static_cast<const char*>(L.P) + static_cast<int64_t>(m0) * 2;
+  const char* U = static_cast<const char*>(L.U);
+  const int64_t p_row = static_cast<int64_t>(L.ldp) * 2, u_row = static_cast<int64_t>(L.d_out) * 2;
+
+  // Copies step `step` into stage `stage`: copy q of wave w fills 1 KiB
+  // block q * 8 + w (P blocks first, then U blocks), rows 2 b and 2 b + 1 of
+  // its operand (b the block's index within the operand); lane l writes slot
+  // l % 32 of row 2 b + l / 32. Block indices of a wave share their parity,
+  // so each lane's byte offset within its row pair is fixed.
+  const int lr = lane >> 5, lc = lane & 31;
+  const int sw = kmajor_slot(2 * (wave & 1) + lr, lc) * 16;  // the swizzle is an involution
+  const int off_p = lr * static_cast<int>(p_row) + sw, off_u = lr * static_cast<int>(u_row) + sw;
+  auto issue = [&](int step, int stage) {
+    char* sb = smem + stage * kStageBytes;
+    const int nt = nt0 + step / kr, k0 = (step % kr) * BK;
+    const char* Pb = P + k0 * p_row;
+    const char* Ub = U + k0 * u_row + static_cast<int64_t>(nt) * kRow;
+#pragma unroll
+    for (int q = 0; q < kCopies; ++q) {
+      const int blk = q * 8 + wave;
+      const char* src = q < kCopies / 2 ? Pb + 2 * blk * p_row + off_p
+                                        : Ub + 2 * (blk - kBlocks) * u_row + off_u;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(sb + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  // lane: columns n + 32 nb; registers i: rows 8 (i / 4) + 4 kh + i % 4 of
+  // each 32-row block mb. W is updated one row block at a time, the next
+  // block's load in flight while the current one is stored, through a buffer
+  // resource on the wave's 128 rows: one per-lane offset, the rest uniform.
+  const __amdgpu_buffer_rsrc_t w_rs =
+      tile_rsrc(L.W + static_cast<int64_t>(m0 + 128 * wm) * L.d_out);
+  const uint32_t row4 = static_cast<uint32_t>(L.d_out) * 4u;
+  const uint32_t w_lane = static_cast<uint32_t>(4 * kh) * row4 +
+                          static_cast<uint32_t>(64 * wn + r32) * 4u;
+  auto w_soff = [&](int nt, int mb, int i) {
+    return __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(32 * mb + 8 * (i >> 2) + (i & 3)) * row4 +
+        static_cast<uint32_t>(nt) * (kBigN * 4u));
+  };
+  typedef float WBlock[2][16];
+  auto load_w = [&](int nt, int mb, WBlock& w) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        w[nb][i] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(w_rs, w_lane + 128u * nb, w_soff(nt, mb, i), 0));
+  };
+  Acc<4, 2> acc;
+  auto store_w = [&](int nt, int mb, const WBlock& w) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(uint32_t, fmaf(-a.lr, acc.v[mb][nb][i], w[nb][i])), w_rs,
+            w_lane + 128u * nb, w_soff(nt, mb, i), 0);
+  };
+
+  acc.zero();
+  if (n_steps > 0) issue(0, 0);
+  WBlock w0, w1;
+  for (int s = 0; s < n_steps; ++s) {
+    wait_vm(0);
+    lds_barrier();  // step s landed for every wave; step s - 1's reads are done
+    if (s + 1 < n_steps) issue(s + 1, (s + 1) & 1);
+    const bool last = s % kr == kr - 1;
+    const int nt = nt0 + s / kr;
+    if (last) load_w(nt, 0, w0);
+    const char* sP = smem + (s & 1) * kStageBytes;
+    const char* sU = sP + kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) af[mb] = frag_kmajor(sP, 16 * kk, 128 * wm + 32 * mb, lane);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bfr[nb] = frag_kmajor(sU, 16 * kk, 64 * wn + 32 * nb, lane);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb],
+                                                                 acc.v[mb][nb], 0, 0, 0);
+    }
+    if (last) {
+      load_w(nt, 1, w1);
+      store_w(nt, 0, w0);
+      load_w(nt, 2, w0);
+      store_w(nt, 1, w1);
+      load_w(nt, 3, w1);
+      store_w(nt, 2, w0);
+      store_w(nt, 3, w1);
+      acc.zero();
+    }
+  }
+}
+
 // ---------------------------------------------------------- philox stream --
 
 __global__ __launch_bounds__(kThreads) void philox_normals_kernel(
@@ -1406,6 +1581,10 @@ hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
 
 hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
+  if (a.big) {
+    hipLaunchKernelGGL(back_big_kernel, g, dim3(2 * kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.res_tiles > 0) {
     if (!bf16_in) {
       if (a.full) hipLaunchKernelGGL((back_res_kernel<float, true, true>), g, b, 0, s, a);

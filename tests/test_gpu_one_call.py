@@ -53,6 +53,10 @@ CASES = {
                                    B=3, T=8, r=16),
     "groups_bf16": W.custom_workload("o_groups_bf16", 47, [(32, 6400), (32, 6400)],
                                      B=33, T=8, r=16),
+    # T at least 8 r: products stored by the norm pass, summed in the final
+    # pass
+    "hat_bf16": W.custom_workload("o_hat_bf16", 49, [(200, 136), (72, 40)], B=3,
+                                  T=400, r=40),
     # the large norm and sum kernel
     "samp_big_bf16": W.custom_workload("o_samp_big_bf16", 48, [(128, 256), (64, 512)],
                                        B=3, T=128, r=256),

@@ -131,6 +131,24 @@ CASES = {
                                             B=2, T=64, r=256),
     "samp_big_groups_bf16": W.custom_workload("samp_big_groups_bf16", 31,
                                               [(32, 10240)], B=16, T=64, r=256),
+    # the large back-projection kernel (d_in, d_out multiples of 256, r of 64
+    # over one 128-step): two layers; r = 192; more than one round of
+    # blocks, so that each block sweeps a run of two column tiles
+    "back_big_bf16": W.custom_workload("back_big_bf16", 32, [(256, 512), (512, 256)],
+                                       B=2, T=64, r=256),
+    "back_big_r192_bf16": W.custom_workload("back_big_r192_bf16", 33, [(256, 256)],
+                                            B=2, T=64, r=192),
+    "back_big_runs_bf16": W.custom_workload("back_big_runs_bf16", 34, [(4096, 8192)],
+                                            B=2, T=64, r=256),
+    # T at least 8 r: the norm pass stores every sample's product and the
+    # final pass sums them weighted by the clip factors (no second pass over
+    # dY); with the large norm kernel, the regular one, and fp32
+    "hat_big_bf16": W.custom_workload("hat_big_bf16", 35, [(128, 256), (64, 512)],
+                                      B=3, T=2048, r=256),
+    "hat_bf16": W.custom_workload("hat_bf16", 36, [(200, 136), (72, 40)], B=2,
+                                  T=512, r=40),
+    "hat_fp32": W.custom_workload("hat_fp32", 37, [(37, 29), (29, 53)], B=2, T=256,
+                                  r=7, dtype="fp32"),
     # fewer tiles: sum groups of 2 samples (accumulator rescaled between
     # them), with a single-sample last group
     "groups4_bf16": W.custom_workload("groups4_bf16", 22,
