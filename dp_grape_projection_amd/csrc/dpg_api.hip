@@ -238,7 +238,8 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // 8-wave block per CU. The K steps per block minimise an estimate of the
   // time in steps, max(work / CUs, longest block), plus the split partials
   // (written and read back) at the bytes one step moves per CU.
-  p.big = kProjBig && dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN;
+  p.big = kProjBig && dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN &&
+          static_cast<uint64_t>(B) * r * p.ldt * 2 < (1ull << 32);  // Xt stores: 32-bit offsets
   for (int l = 0; l < n_layers; ++l)
     if (layers[l].d_in % kBigK != 0) p.big = false;
   int64_t big_sps = 0;

@@ -266,9 +266,12 @@ __device__ __forceinline__ void load_batch(f32x4 (&buf)[kSumBatch], const float*
 // operand tiles (256 rows x 128 bytes each) are copied into LDS by direct
 // global-to-LDS loads, one step ahead of the matrix cores (two stages). A
 // row's eight 16-byte chunks are stored XOR-swizzled by a function of the row
-// so that the 32 rows an MFMA operand read touches spread over the banks.
-// Waves are 2 (j) x 4 (n); each computes 128 x 64 with 32x32x16 MFMAs, its B
-// operand rows read in the order that gives every lane two consecutive n.
+// so that the rows an MFMA operand read touches spread over the banks: a
+// 16-byte LDS read serves 16 lanes (256 bytes) at a time, and rows of 128
+// bytes put even rows in one half of the 64 banks and odd rows in the other,
+// so chunk c of row R goes to slot c ^ (R / 2 mod 8), which gives the 16
+// consecutive rows of a lane group 16 different bank ranges. Waves are 2 (j)
+// x 4 (n); each computes 128 x 64 with 32x32x16 MFMAs.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
@@ -289,8 +292,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // BK: K step (elements); S: pipeline stages. Rows of a stage are BK * 2 bytes
-// in CH chunks of 16 bytes; chunk c of row R sits in slot c ^ f(R) with
-// f(R) = R (P tiles) or R / 2 (A tiles), modulo CH.
+// in CH chunks of 16 bytes; chunk c of row R sits in slot c ^ (R / 2 mod CH).
 template <int BK, int S>
 __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArgs a) {
   constexpr int kRowBytes = BK * 2;
@@ -322,8 +324,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   const char* Pb = static_cast<const char*>(L.P) + static_cast<int64_t>(j0) * L.ldp * 2;
   const char* Ab = static_cast<const char*>(L.A) + static_cast<int64_t>(n0) * L.d_in * 2;
   const int64_t p_row = static_cast<int64_t>(L.ldp) * 2, a_row = static_cast<int64_t>(L.d_in) * 2;
-  auto slot_p = [](int R, int c) { return c ^ (R & (CH - 1)); };
-  auto slot_a = [](int R, int c) { return c ^ ((R >> 1) & (CH - 1)); };
+  // 16 consecutive rows (the rows a 16-lane group reads) cover both halves
+  // of the 64 banks with 8 different slots each
+  auto slot_p = [](int R, int c) { return c ^ ((R >> 1) & (CH - 1)); };
+  auto slot_a = slot_p;
 
   // Copies K step `step` into stage `stage`: copy q of wave w fills row
   // block g = q * 8 + w (P blocks first, then A blocks); lane l writes slot
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const int n = 64 * wn + 2 * r32 + nb;
+        const int n = 64 * wn + 32 * nb + r32;
         bfr[nb] = *reinterpret_cast<const bf16x8*>(sA + n * kRowBytes + slot_a(n, c) * 16);
       }
 #pragma unroll
@@ -382,37 +386,50 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
     }
   }
 
-  // lane: columns n, n + 1; registers i: rows 8 (i / 4) + 4 kh + i % 4
-  const int n = n0 + 64 * wn + 2 * r32;
+  // lane: column n0 + 64 wn + 32 nb + r32; registers i: rows
+  // 8 (i / 4) + 4 kh + i % 4 of each 32-row block. Stores go through buffer
+  // resources: one per-lane offset and uniform row offsets (the plan keeps
+  // Xt and a split partial within 32-bit byte offsets).
   if (L.splits == 1) {
-    bf16* Xt = static_cast<bf16*>(L.Xt);
-    const int bi = n / a.T, t = n - bi * a.T;
-    const bool pair = t + 1 < a.T;  // n + 1 in the same sample
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(L.Xt);
+    const uint32_t row2 = static_cast<uint32_t>(a.ldt) * 2u;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = n0 + 64 * wn + 32 * nb + r32;
+      const int bi = n / a.T, t = n - bi * a.T;
+      const uint32_t lo = (static_cast<uint32_t>(bi * a.r + j0 + 128 * wm + 4 * kh)) * row2 +
+                          static_cast<uint32_t>(t) * 2u;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = j0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * kh + (i & 3);
-        bf16* dst = Xt + (static_cast<int64_t>(bi) * a.r + j) * a.ldt + t;
-        if (pair && (t & 1) == 0) {
-          const bf16 v2[2] = {from_float<bf16>(acc.v[mb][0][i]), from_float<bf16>(acc.v[mb][1][i])};
-          *reinterpret_cast<uint32_t*>(dst) = __builtin_bit_cast(uint32_t, v2);
-        } else {
-          dst[0] = from_float<bf16>(acc.v[mb][0][i]);
-          const int t1 = pair ? t + 1 : 0, b1 = pair ? bi : bi + 1;
-          Xt[(static_cast<int64_t>(b1) * a.r + j) * a.ldt + t1] = from_float<bf16>(acc.v[mb][1][i]);
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bf16 v = from_float<bf16>(acc.v[mb][nb][i]);
+          __builtin_amdgcn_raw_buffer_store_b16(
+              __builtin_bit_cast(unsigned short, v), rs, lo,
+              __builtin_amdgcn_readfirstlane(
+                  static_cast<uint32_t>(32 * mb + 8 * (i >> 2) + (i & 3)) * row2),
+              0);
         }
-      }
+    }
   } else {
-    float* part = L.part + static_cast<int64_t>(split) * a.r * BT;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(
+        L.part + (static_cast<int64_t>(split) * a.r + j0 + 128 * wm) * BT);
+    const uint32_t row4 = static_cast<uint32_t>(BT) * 4u;
+    const uint32_t lo = static_cast<uint32_t>(4 * kh) * row4 +
+                        static_cast<uint32_t>(n0 + 64 * wn + r32) * 4u;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = j0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * kh + (i & 3);
-        *reinterpret_cast<f32x2*>(part + static_cast<int64_t>(j) * BT + n) =
-            f32x2{acc.v[mb][0][i], acc.v[mb][1][i]};
-      }
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = acc.v[mb][nb][i];
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, v), rs, lo + 128u * nb,
+              __builtin_amdgcn_readfirstlane(
+                  static_cast<uint32_t>(32 * mb + 8 * (i >> 2) + (i & 3)) * row4),
+              0);
+        }
   }
 }
 
@@ -744,7 +761,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   const char* Xt = static_cast<const char*>(L.Xt);
   const char* dY = static_cast<const char*>(L.dY);
   const int64_t x_row = static_cast<int64_t>(a.ldt) * 2, y_row = static_cast<int64_t>(L.d_out) * 2;
-  auto slot_a = [](int R, int c) { return c ^ (R & (CHA - 1)); };
+  // 16 consecutive rows cover both halves of the 64 banks with 8 slots each
+  auto slot_a = [](int R, int c) { return c ^ ((R >> 1) & (CHA - 1)); };
 
   // Copies step `step` into stage `stage`: copy q of wave w fills 1 KiB
   // block q * 8 + w (Xt blocks of 8 rows first, then dY blocks of 2 rows);
