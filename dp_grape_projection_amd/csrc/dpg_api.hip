@@ -600,10 +600,12 @@ int enqueue_back(const dpg_layer_param* params, int l0, int l1, int32_t r,
     if (static_cast<uint64_t>(r) * std::max<int64_t>(ldp_of(l), params[l].d_out) *
             elem_size(dtype) >= (1ull << 31))
       b.off32 = 0;
-  // every tile and step full: d_in, d_out whole tiles, r whole steps
+  // every tile and step full: d_in, d_out whole tiles, r whole steps, W
+  // rows 8-byte aligned
   b.full = pair && b.off32 && r % step_of(dtype) == 0;
   for (int l = l0; l < l1; ++l)
-    if (params[l].d_in % kTileM != 0 || params[l].d_out % kBackN != 0) b.full = 0;
+    if (params[l].d_in % kTileM != 0 || params[l].d_out % kBackN != 0 || !aligned(params[l].W, 8))
+      b.full = 0;
   return timed(K_BACK, s, [&] { return launch_back(b, bf16, pair, s); });
 }
 

@@ -39,6 +39,12 @@ __device__ __forceinline__ int find_layer(const L* layers, int n, int b) {
 }
 
 // Sum over the 64 lanes of a wave (butterfly, deterministic).
+// Caller pointers are only element aligned; vector accesses to them are
+// taken when the pointer allows them (the test is uniform per layer).
+__device__ __forceinline__ bool is_aligned(const void* p, unsigned bytes) {
+  return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -494,7 +500,7 @@ __device__ __forceinline__ void store_tile(float* dst, const Acc<Tl::MB, Tl::NB>
   static_assert(Tl::MB == 1 && (NB == 4 || NB == 2) && Tl::WGN == 1, "4 x 1 waves");
   const int wm = Tl::wave_m(wave);
   const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's NB columns
-  const bool vec = (d_out % NB) == 0 && nq + NB - 1 < d_out;
+  const bool vec = (d_out % NB) == 0 && nq + NB - 1 < d_out && is_aligned(dst, NB * 4);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = j0 + Tl::acc_row(wm, 0, i, lane);
@@ -949,7 +955,9 @@ __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
   const int64_t e0 = 4ll * c;
   if (e0 >= L.n_elem) return;
   float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if ((L.n_elem & 3) == 0) {
+  const bool vec = (L.n_elem & 3) == 0 && is_aligned(L.part, 16) && is_aligned(L.out, 16) &&
+                   (!ADAM || (is_aligned(L.m, 16) && is_aligned(L.v, 16)));
+  if (vec) {
     // The partials are loaded up to kSumBatch at a time, all in flight
     // together, with the moments and the noise computed while they arrive;
     // they are added in group order.
@@ -1061,7 +1069,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepArgs a) {
   const int64_t e0 = 4ll * c;
   if (e0 >= L.n_elem) return;
   T* U = static_cast<T*>(L.U);
-  if ((L.n_elem & 3) == 0) {
+  if ((L.n_elem & 3) == 0 && is_aligned(L.g, 16) && is_aligned(L.m, 16) && is_aligned(L.v, 16)) {
     const f32x4 g = *reinterpret_cast<const f32x4*>(L.g + e0);
     f32x4 m = *reinterpret_cast<const f32x4*>(L.m + e0);
     f32x4 v = *reinterpret_cast<const f32x4*>(L.v + e0);
@@ -1110,7 +1118,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = Tl::wave_m(wave);
   const int nq = n0 + Tl::acc_col(0, 0, lane);  // this lane's 2 columns
-  const bool vec = (L.d_out & 1) == 0;
+  const bool vec = (L.d_out & 1) == 0 && is_aligned(L.W, 8);
 
   // W rows of this lane (2 consecutive columns each), fetched before the
   // operands so that both are in flight together.
@@ -1203,7 +1211,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = Tl::wave_m(wave), wn = Tl::wave_n(wave);
   const int lq = Tl::acc_col(0, 0, lane);  // this lane's 2 columns in a tile
-  const bool vec = (L.d_out & 1) == 0;
+  const bool vec = (L.d_out & 1) == 0 && is_aligned(L.W, 8);
   T* sA = smem;
   T* sB = smem + Tl::BM * Tl::S;
 

@@ -60,7 +60,13 @@ typedef enum {
 } dpg_status;
 
 /* Element type of the activations A and output gradients dY. Everything
- * else (G_priv, W, m, v, sample norms) is fp32. */
+ * else (G_priv, W, m, v, sample norms) is fp32.
+ *
+ * Device pointers need only the alignment of their element type. The fast
+ * paths (the 256 x 256 tile kernels and every vector access to a caller
+ * tensor) are taken for pointers 16-byte aligned (8 for W), as hipMalloc and
+ * torch allocations are; other pointers take element-wise forms with the
+ * same results within the stated tolerances. */
 typedef enum { DPG_FP32 = 0, DPG_BF16 = 1 } dpg_dtype;
 
 /* One linear layer's inputs to dpg_project_clip_noise. */

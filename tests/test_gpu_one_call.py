@@ -149,3 +149,72 @@ def test_prepared_step_one_call_equals_two_calls():
                    + _np(ms) + _np(vs))
     for a, b in zip(*out):
         np.testing.assert_array_equal(a, b)
+
+
+# Caller tensors that start one element past an aligned address: the
+# large-tile kernels (which need 16-byte rows) and every vector access to a
+# caller pointer step aside for their element-wise forms. The bf16 case has
+# shapes that take all three large-tile kernels when aligned.
+UNALIGNED = {
+    "big_bf16": W.custom_workload("u_big_bf16", 50, [(256, 512), (512, 256)], B=4,
+                                  T=128, r=256),
+    "fp32": W.custom_workload("u_fp32", 51, [(64, 96), (96, 40)], B=2, T=24, r=16,
+                              dtype="fp32"),
+}
+
+
+def _offset_copy(t):
+    """A copy of t whose data starts one element past t's allocation start."""
+    import torch
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("name", list(UNALIGNED))
+def test_unaligned_caller_tensors(name):
+    import torch
+    import dp_grape_projection_amd as dpg
+    wl = UNALIGNED[name]
+    print(f"[unaligned] {name}: {len(wl.layers)} layers B={wl.B} T={wl.T} r={wl.r} "
+          f"{wl.dtype}", flush=True)
+    host, orc, state = make_case(wl)
+    A = [_offset_copy(to_device(wl, a)) for a, _ in host]
+    dY = [_offset_copy(to_device(wl, d)) for _, d in host]
+    assert all(t.data_ptr() % 16 != 0 for t in A + dY)
+    ids = [L.layer_id for L in wl.layers]
+    hyper = dict(r=wl.r, clip_C=wl.clip_C, sigma=wl.sigma, seed=wl.seed)
+    adam = dict(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps)
+    W1, m1, v1 = [[_offset_copy(x) for x in xs] for xs in _state(state)]
+    W2, m2, v2 = [[_offset_copy(x) for x in xs] for xs in _state(state)]
+    G1, n1 = dpg.dpg_private_step(A, dY, W1, m1, v1, step=1, proj_step=1,
+                                  layer_ids=ids, **hyper, **adam)
+    G2 = [_offset_copy(torch.zeros(wl.r, L.d_out, device="cuda")) for L in wl.layers]
+    G2, n2 = dpg.dpg_project_clip_noise(A, dY, step=1, proj_step=1, layer_ids=ids,
+                                        G_priv=G2, **hyper)
+    dpg.dpg_adam_backproject(G2, W2, m2, v2, wl.r, seed=wl.seed, step=1, proj_step=1,
+                             layer_ids=ids, dtype=torch_dtype(wl), **adam)
+    torch.cuda.synchronize()
+    tol = TOL[wl.dtype]
+    want = oracle.project_clip_noise(orc, wl.r, wl.clip_C, wl.sigma, wl.seed, 1, 1)
+    params = [{"W": s[0].astype(np.float64), "m": s[1].astype(np.float64),
+               "v": s[2].astype(np.float64), "G_priv": g.astype(np.float64),
+               "layer_id": L.layer_id}
+              for s, g, L in zip(state, _np(G1), wl.layers)]
+    upd = oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2, wl.eps,
+                                  wl.seed, 1, 1)
+    for G, n, Ws, ms, vs in ((G1, n1, W1, m1, v1), (G2, n2, W2, m2, v2)):
+        e_n = rel_fro(n.cpu().numpy(), want["norms"])
+        e_g = max(rel_fro(g, w) for g, w in zip(_np(G), want["G_priv"]))
+        e_w = max(rel_fro(w.astype(np.float64) - s[0], u["dW"])
+                  for w, s, u in zip(_np(Ws), state, upd))
+        e_m = max(rel_fro(m, u["m"]) for m, u in zip(_np(ms), upd))
+        e_v = max(rel_fro(v, u["v"]) for v, u in zip(_np(vs), upd))
+        print(f"[unaligned] {name}: norms {e_n:.2e} G_priv {e_g:.2e} dW {e_w:.2e} "
+              f"m {e_m:.2e} v {e_v:.2e}", flush=True)
+        assert max(e_n, e_g, e_w, e_m, e_v) <= tol
+    # the one-call and two-call forms agree bit for bit here too
+    assert torch.equal(n1, n2)
+    for a, b in zip(G1 + W1 + m1 + v1, G2 + W2 + m2 + v2):
+        assert torch.equal(a, b)
