@@ -140,6 +140,9 @@ CASES = {
                                             B=2, T=64, r=192),
     "back_big_runs_bf16": W.custom_workload("back_big_runs_bf16", 34, [(4096, 8192)],
                                             B=2, T=64, r=256),
+    # runs of three column tiles over 34: the last run holds one tile
+    "back_big_ragged_run_bf16": W.custom_workload("back_big_ragged_run_bf16", 38,
+                                                  [(4096, 8704)], B=2, T=64, r=256),
     # T at least 8 r: the norm pass stores every sample's product and the
     # final pass sums them weighted by the clip factors (no second pass over
     # dY); with the large norm kernel, the regular one, and fp32
