@@ -238,8 +238,11 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // 8-wave block per CU. The K steps per block minimise an estimate of the
   // time in steps, max(work / CUs, longest block), plus the split partials
   // (written and read back) at the bytes one step moves per CU.
+  // (its epilogue stores use 32-bit offsets: all of Xt, and 256 rows of a
+  // split partial)
   p.big = kProjBig && dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN &&
-          static_cast<uint64_t>(B) * r * p.ldt * 2 < (1ull << 32);  // Xt stores: 32-bit offsets
+          static_cast<uint64_t>(B) * r * p.ldt * 2 < (1ull << 32) &&
+          static_cast<uint64_t>(BT) * 4 * kBigM < (1ull << 32);
   for (int l = 0; l < n_layers; ++l)
     if (layers[l].d_in % kBigK != 0) p.big = false;
   int64_t big_sps = 0;
@@ -361,8 +364,10 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // the launches, with the rounds of resident blocks counted in K steps
   // (plus two per block for the pipeline's fill).
   p.has_samp_big = kSampBig && dtype == DPG_BF16 && r % kBigM == 0 && T % kSampBigK == 0;
-  for (int l = 0; l < n_layers; ++l)
-    if (layers[l].d_out % kBigN != 0) p.has_samp_big = false;
+  for (int l = 0; l < n_layers; ++l)  // (stored products: 32-bit offsets over 256 rows)
+    if (layers[l].d_out % kBigN != 0 ||
+        static_cast<uint64_t>(layers[l].d_out) * 4 * kBigM >= (1ull << 32))
+      p.has_samp_big = false;
   if (p.has_samp_big) {
     SampPlan& b = p.samp_big;
     b.big = true;
@@ -536,7 +541,8 @@ int enqueue_back(const dpg_layer_param* params, int l0, int l1, int32_t r,
   for (int l = l0; l < l1; ++l)
     if (params[l].d_in % kBigM != 0 || params[l].d_out % kBigN != 0 ||
         !aligned(params[l].W, 16) || !aligned(P_of(l), 16) || !aligned(U_of(l), 16) ||
-        (ldp_of(l) * elem_size(dtype)) % 16 != 0)
+        (ldp_of(l) * elem_size(dtype)) % 16 != 0 ||
+        static_cast<uint64_t>(params[l].d_out) * 4 * kBigM >= (1ull << 32))  // W: 32-bit offsets
       b.big = 0;
   if (b.big) {
     int64_t best = -1, max_nt = 1;
