@@ -43,7 +43,10 @@ def parse():
     ap.add_argument("--timing-steps", type=int, default=50,
                     help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=3,
+                    help="least number of oracle runs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle runs continue until this much time has passed")
     ap.add_argument("--no-streaming", action="store_true",
                     help="skip timing the two-call and streaming forms of "
                          "the step")
@@ -122,8 +125,9 @@ def kernel_work(wl):
     return w
 
 
-def cpu_baseline(wl, host, state, reps):
-    """The float64 oracle on the full step of the same workload."""
+def cpu_baseline(wl, host, state, reps, seconds):
+    """The float64 oracle on the full step of the same workload: at least
+    `reps` runs, and more until `seconds` have passed (at most 200 runs)."""
     import numpy as np
     import oracle
     import workloads as W
@@ -135,7 +139,7 @@ def cpu_baseline(wl, host, state, reps):
     orc = [{"A": W.as_float64(wl, a), "dY": W.as_float64(wl, d),
             "layer_id": L.layer_id} for (a, d), L in zip(host, wl.layers)]
     times = []
-    for _ in range(reps):
+    while len(times) < reps or (sum(times) < seconds and len(times) < 200):
         t0 = time.perf_counter()
         res = oracle.project_clip_noise(orc, wl.r, wl.clip_C, wl.sigma,
                                         wl.seed, wl.step, wl.proj_step)
@@ -150,7 +154,8 @@ def cpu_baseline(wl, host, state, reps):
             "cores": int(threads), "kind": "oracle",
             "sample": f"full step of {wl.name} ({wl.B} samples, "
                       f"{len(wl.layers)} layers), float64 numpy, median of "
-                      f"{reps} runs of {[round(x, 2) for x in times]} s"}
+                      f"{len(times)} runs ({sum(times):.1f} s in all; "
+                      f"{min(times):.2f} to {max(times):.2f} s each)"}
 
 
 def main():
@@ -339,7 +344,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and host is not None:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, host, state, args.cpu_reps)
+        cpu = cpu_baseline(wl, host, state, args.cpu_reps, args.cpu_seconds)
 
     layers = "->".join([str(wl.layers[0].d_in)] + [str(L.d_out) for L in wl.layers]) \
         if all(a.d_out == b.d_in for a, b in zip(wl.layers, wl.layers[1:])) \
