@@ -3,6 +3,7 @@
 // is allocated here and no state survives a call (apart from the calling
 // thread's last error message).
 #include <algorithm>
+#include <map>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -249,19 +250,27 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   if (p.big) {
     const int64_t tiles = (r / kBigM) * (BT / kBigN), cus = target / 2;
     int64_t work = 0, max_steps = 1;
+    std::map<int64_t, int64_t> n_of_steps;  // K steps of a layer -> layers
     for (int l = 0; l < n_layers; ++l) {
       work += tiles * (layers[l].d_in / kBigK);
       max_steps = std::max<int64_t>(max_steps, layers[l].d_in / kBigK);
+      ++n_of_steps[layers[l].d_in / kBigK];
     }
+    // candidates: the K steps per block that split the longest layer into
+    // 1, 2, ... (at most 1024) parts, longest first
     double best = -1.0;
-    for (int64_t sps = max_steps; sps >= 1; --sps) {
+    int64_t prev = -1;
+    for (int64_t parts = 1; parts <= std::min<int64_t>(max_steps, 1024); ++parts) {
+      const int64_t sps = ceil_div(max_steps, parts);
+      if (sps == prev) continue;
+      prev = sps;
       int64_t blocks = 0, longest = 0;
       double part = 0.0;
-      for (int l = 0; l < n_layers; ++l) {
-        const int64_t steps = layers[l].d_in / kBigK, sp = ceil_div(steps, sps);
-        blocks += tiles * sp;
+      for (const auto& kv : n_of_steps) {
+        const int64_t steps = kv.first, sp = ceil_div(steps, sps);
+        blocks += tiles * sp * kv.second;
         longest = std::max<int64_t>(longest, ceil_div(steps, sp));
-        if (sp > 1) part += 2.0 * sp * r * BT * 4;
+        if (sp > 1) part += 2.0 * sp * r * BT * 4 * kv.second;
       }
       const double t = static_cast<double>(blocks <= cus ? longest
                                                          : std::max(ceil_div(work, cus), longest)) +
@@ -390,7 +399,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       return t;
     };
     int64_t best = -1;
-    for (int64_t pb = 1; pb <= B; ++pb) {
+    for (int64_t pb = 1; pb <= std::min<int64_t>(B, kSumMaxGroup); ++pb) {
       const int64_t cost = step_rounds(pb);
       if (best < 0 || cost <= best) {
         best = cost;
