@@ -45,6 +45,11 @@ CASES = {
                                    B=2, T=128, r=128),
     "long_t_bf16": W.custom_workload("s_long_t_bf16", 34, [(64, 96)], B=2,
                                      T=300, r=160),
+    # r and B*T whole 256 x 256 tiles, d_in whole K steps: the per-layer
+    # projection takes the large-tile kernel, the update the large-tile
+    # back-projection
+    "big_tiles_bf16": W.custom_workload("s_big_tiles_bf16", 35,
+                                        [(256, 512), (512, 256)], B=2, T=256, r=256),
 }
 
 
