@@ -16,7 +16,11 @@ calls (dpg_project_clip_noise then dpg_adam_backproject) and in its
 streaming form (dpg_project_layer per layer, then dpg_clip_sum_noise and the
 update).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mlp4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dec24]
+
+The default workload is dec24 (24 decoder blocks of q, k, v, o 2048 x 2048
+and MLP 2048 <-> 8192, B = 16, T = 512, r = 512, bf16), the largest one; the
+others (tiny, mlp4, enc12, long1) are available with --workload.
 """
 import argparse
 import json
@@ -37,15 +41,15 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mlp4")
-    ap.add_argument("--timing-steps", type=int, default=50,
+    ap.add_argument("--workload", default="dec24")
+    ap.add_argument("--timing-steps", type=int, default=20,
                     help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3,
+    ap.add_argument("--cpu-reps", type=int, default=2,
                     help="least number of oracle runs")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle runs continue until this much time has passed")
     ap.add_argument("--no-streaming", action="store_true",
                     help="skip timing the two-call and streaming forms of "
@@ -53,14 +57,16 @@ def parse():
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw A, dY, W on the GPU (workloads.device_layer_inputs); "
                          "the default for enc12, dec24 and long1, whose host "
-                         "draws would take minutes. Skips the CPU oracle.")
+                         "draws would take minutes. The CPU oracle then runs on "
+                         "one block at two batch sizes and is extrapolated.")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the steps, copy a buffer of this many MiB "
                          "three times (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mlp4_hbm_traffic.md")
+def traffic_summary(workload):
+    return os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
 
 
 def kernel_source_digest():
@@ -83,7 +89,7 @@ def measured_traffic(kernel, workload):
     (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None when
     there is none for this workload or the kernels changed since."""
     try:
-        with open(TRAFFIC_SUMMARY) as fh:
+        with open(traffic_summary(workload)) as fh:
             text = fh.read()
         block = text.split("```json", 1)[1].split("```", 1)[0]
         data = json.loads(block)
@@ -125,33 +131,85 @@ def kernel_work(wl):
     return w
 
 
-def cpu_baseline(wl, host, state, reps, seconds):
-    """The float64 oracle on the full step of the same workload: at least
-    `reps` runs, and more until `seconds` have passed (at most 200 runs)."""
-    import numpy as np
-    import oracle
-    import workloads as W
+def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    orc = [{"A": W.as_float64(wl, a), "dY": W.as_float64(wl, d),
-            "layer_id": L.layer_id} for (a, d), L in zip(host, wl.layers)]
+        return len(os.sched_getaffinity(0))
+
+
+def _time_oracle_step(wl, orc, state, reps, seconds):
+    """Wall times of the unchanged float64 oracle on one full step of the
+    layers in `orc` (projection, norms, clip, sum, noise, Adam and the
+    back-projection): at least `reps` runs, more until `seconds` passed."""
+    import oracle
     times = []
     while len(times) < reps or (sum(times) < seconds and len(times) < 200):
         t0 = time.perf_counter()
         res = oracle.project_clip_noise(orc, wl.r, wl.clip_C, wl.sigma,
                                         wl.seed, wl.step, wl.proj_step)
-        params = [{"W": s[0], "m": s[1], "v": s[2], "G_priv": g,
-                   "layer_id": L.layer_id}
-                  for s, g, L in zip(state, res["G_priv"], wl.layers)]
+        params = [{"W": st[0], "m": st[1], "v": st[2], "G_priv": g,
+                   "layer_id": o["layer_id"]}
+                  for st, g, o in zip(state, res["G_priv"], orc)]
         oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2,
                                 wl.eps, wl.seed, wl.step, wl.proj_step)
         times.append(time.perf_counter() - t0)
+    return times
+
+
+def cpu_baseline_blocks(wl, A, dY, Wd, reps, seconds):
+    """The float64 oracle on a bounded sample of a block-structured workload
+    whose inputs live in device memory: the first block (6 layers) at B = 1
+    and at B = 4, with the workload's T, r, shapes and values (host copies of
+    the device draws). Every block has the same shapes, and the oracle's
+    work splits into a per-step part (P, noise, Adam, back-projection) and a
+    per-sample part (the materialised per-sample gradients and their
+    projections), so the full step takes n_blocks x (t_fixed + B t_sample),
+    with t_sample = (t(4) - t(1)) / 3 and t_fixed = t(1) - t_sample."""
+    import numpy as np
+    per = 6
+    n_blk = len(wl.layers) // per
+    sub = list(range(per))
+
+    def host(t, b):
+        return t[:b].float().cpu().numpy().astype(np.float64)
+
+    state = [(Wd[l].cpu().numpy().astype(np.float64),
+              np.zeros((wl.r, wl.layers[l].d_out)),
+              np.zeros((wl.r, wl.layers[l].d_out))) for l in sub]
+    med = {}
+    runs = {}
+    for b in (1, 4):
+        orc = [{"A": host(A[l], b), "dY": host(dY[l], b),
+                "layer_id": wl.layers[l].layer_id} for l in sub]
+        t = _time_oracle_step(wl, orc, state, reps, seconds / 2)
+        med[b] = statistics.median(t)
+        runs[b] = len(t)
+    t_sample = max(med[4] - med[1], 0.0) / 3.0
+    t_fixed = med[1] - t_sample
+    t_step = n_blk * (t_fixed + wl.B * t_sample)
+    return {"value": round(wl.B / t_step, 5), "unit": "samples/s",
+            "cores": int(_oracle_threads()), "kind": "oracle",
+            "sample": f"float64 numpy oracle, full step of block 0 of {n_blk} "
+                      f"({per} layers, T={wl.T}, r={wl.r}) at B=1 (median of "
+                      f"{runs[1]} runs: {med[1]:.2f} s) and B=4 (median of "
+                      f"{runs[4]} runs: {med[4]:.2f} s); extrapolated to the "
+                      f"{len(wl.layers)}-layer step at B={wl.B} as {n_blk} x "
+                      f"({t_fixed:.2f} s + {wl.B} x {t_sample:.3f} s) = "
+                      f"{t_step:.1f} s"}
+
+
+def cpu_baseline(wl, host, state, reps, seconds):
+    """The float64 oracle on the full step of the same workload: at least
+    `reps` runs, and more until `seconds` have passed (at most 200 runs)."""
+    import workloads as W
+    orc = [{"A": W.as_float64(wl, a), "dY": W.as_float64(wl, d),
+            "layer_id": L.layer_id} for (a, d), L in zip(host, wl.layers)]
+    times = _time_oracle_step(wl, orc, state, reps, seconds)
     t = statistics.median(times)
     return {"value": round(wl.B / t, 3), "unit": "samples/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": int(_oracle_threads()), "kind": "oracle",
             "sample": f"full step of {wl.name} ({wl.B} samples, "
                       f"{len(wl.layers)} layers), float64 numpy, median of "
                       f"{len(times)} runs ({sum(times):.1f} s in all; "
@@ -254,6 +312,9 @@ def main():
         dpg.timing_enable(False)
     work = kernel_work(wl)
     peak_flops = BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    # the matrix cores bound a kernel whose algorithmic flops per algorithmic
+    # byte exceed the machine balance (2500 / 8 = 312.5 flop/byte in bf16)
+    ridge = peak_flops * 1e12 / (HBM_PEAK_GBS * 1e9)
     kernels = {}
     for name, (ms, n) in times.items():
         if n == 0:
@@ -261,23 +322,37 @@ def main():
         per_step_launches = n / args.timing_steps
         avg_us = ms * 1e3 / n
         byt, flo = work[name]
-        # one step's work is split evenly over that step's launches
+        # a launch's algorithmic work: one step's work over that step's
+        # launches (the average launch)
         byt_l, flo_l = byt / per_step_launches, flo / per_step_launches
+        gbs = byt_l / (avg_us * 1e-6) / 1e9
+        tfs = flo_l / (avg_us * 1e-6) / 1e12
+        mfma = byt > 0 and flo / byt > ridge
         kernels[name] = {
             "avg_us": round(avg_us, 2), "launches_per_step": per_step_launches,
             "us_per_step": round(avg_us * per_step_launches, 2),
-            "GB/s": round(byt_l / (avg_us * 1e-6) / 1e9, 1),
-            "TFLOP/s": round(flo_l / (avg_us * 1e-6) / 1e12, 2)}
+            "GB/s": round(gbs, 1), "TFLOP/s": round(tfs, 2),
+            "flop_per_byte": round(flo / byt, 1) if byt > 0 else None,
+            "bound": "mfma" if mfma else "hbm",
+            "frac": round(tfs / peak_flops if mfma else gbs / HBM_PEAK_GBS, 4)}
     roof = None
     if kernels:
         dom = max(kernels, key=lambda k: kernels[k]["us_per_step"])
         dk = kernels[dom]
-        roof = {"kernel": dom, "bound": "hbm", "achieved": dk["GB/s"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, wl.name),
-                "mfma_TFLOP/s": dk["TFLOP/s"],
-                "mfma_frac": round(dk["TFLOP/s"] / peak_flops, 4)}
+        byt, flo = work[dom]
+        launches = dk["launches_per_step"]
+        if dk["bound"] == "mfma":
+            roof = {"kernel": dom, "bound": "mfma", "achieved": dk["TFLOP/s"],
+                    "peak": peak_flops, "unit": "TFLOP/s", "frac": dk["frac"]}
+        else:
+            roof = {"kernel": dom, "bound": "hbm", "achieved": dk["GB/s"],
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["frac"]}
+        roof.update({
+            "traffic": measured_traffic(dom, wl.name),
+            "algorithmic_bytes_per_launch": int(byt / launches),
+            "algorithmic_flops_per_launch": float(flo / launches),
+            "avg_launch_us": dk["avg_us"], "launches_per_step": launches,
+            "hbm_GB/s": dk["GB/s"], "ridge_flop_per_byte": round(ridge, 1)})
 
     # The whole step against its algorithmic HBM bytes at the HBM peak.
     step_bytes = sum(b for b, _ in work.values())
@@ -342,9 +417,12 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.no_cpu_baseline and host is not None:
+    if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, host, state, args.cpu_reps, args.cpu_seconds)
+        if host is not None:
+            cpu = cpu_baseline(wl, host, state, args.cpu_reps, args.cpu_seconds)
+        elif len(wl.layers) % 6 == 0:
+            cpu = cpu_baseline_blocks(wl, A, dY, Wd, args.cpu_reps, args.cpu_seconds)
 
     layers = "->".join([str(wl.layers[0].d_in)] + [str(L.d_out) for L in wl.layers]) \
         if all(a.d_out == b.d_in for a, b in zip(wl.layers, wl.layers[1:])) \
@@ -355,7 +433,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-        "data": "synthetic (seeded Gaussian A, dY; Gaussian W%s)" % (
+        "data": "synthetic, seeded: A Gaussian, dY %s, W Gaussian%s" % (
+            "Student-t(3)" if wl.dy_kind.startswith("t3") else "Gaussian",
             ", drawn on the GPU" if device_inputs else ""),
         "config": {"workload": wl.name, "layers": layers, "B": wl.B,
                    "T": wl.T, "r": wl.r, "clip_C": wl.clip_C,

@@ -9,6 +9,8 @@ library has not been built.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import math
 import os
 from typing import List, Optional, Sequence
@@ -163,6 +165,24 @@ def _stream_handle(stream) -> int:
     return stream.cuda_stream
 
 
+def _on_stream(fn):
+    """Runs `fn` with its `stream` argument (when given) as torch's current
+    stream, so that the outputs and temporary workspaces it allocates belong
+    to the stream the library's kernels are enqueued on: the caching
+    allocator then does not hand their memory to other work while those
+    kernels may still use it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        stream = sig.bind(*args, **kw).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return wrapper
+
+
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if workspace is not None:
         _require(workspace, "workspace", torch.uint8)
@@ -201,6 +221,7 @@ def adam_workspace_size(shapes: Sequence, r: int, dtype: torch.dtype,
     return out.value
 
 
+@_on_stream
 def dpg_project_clip_noise(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
                            r: int, clip_C: float, sigma: float, seed: int,
                            step: int, proj_step: Optional[int] = None,
@@ -252,6 +273,7 @@ def dpg_project_clip_noise(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor]
     return G_priv, sample_norms
 
 
+@_on_stream
 def dpg_adam_backproject(G_priv: Sequence[torch.Tensor], W: Sequence[torch.Tensor],
                          m: Sequence[torch.Tensor], v: Sequence[torch.Tensor],
                          r: int, lr: float, beta1: float, beta2: float,
@@ -289,6 +311,7 @@ def dpg_adam_backproject(G_priv: Sequence[torch.Tensor], W: Sequence[torch.Tenso
     return W, m, v
 
 
+@_on_stream
 def dpg_private_step(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
                      W: Sequence[torch.Tensor], m: Sequence[torch.Tensor],
                      v: Sequence[torch.Tensor], r: int, clip_C: float, sigma: float,
@@ -308,6 +331,7 @@ def dpg_private_step(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
     return ps.G_priv, ps.sample_norms
 
 
+@_on_stream
 def dpg_project_layer(A: torch.Tensor, dY: torch.Tensor, r: int, seed: int,
                       proj_step: int, layer_id: int, norm_sq: torch.Tensor,
                       G_hat: Optional[torch.Tensor] = None,
@@ -339,6 +363,7 @@ def dpg_project_layer(A: torch.Tensor, dY: torch.Tensor, r: int, seed: int,
     return G_hat
 
 
+@_on_stream
 def dpg_clip_sum_noise(G_hat: Sequence[torch.Tensor], r: int, clip_C: float,
                        sigma: float, seed: int, step: int, norm_sq: torch.Tensor,
                        layer_ids: Optional[Sequence[int]] = None,
@@ -381,6 +406,7 @@ def dpg_clip_sum_noise(G_hat: Sequence[torch.Tensor], r: int, clip_C: float,
     return G_priv, sample_norms
 
 
+@_on_stream
 def dpg_philox_normals(seed: int, layer_id: int, step_word: int, tag: int,
                        start: int, n: int, device="cuda", words: bool = False,
                        stream=None):
@@ -458,10 +484,22 @@ class PreparedStep:
         self.ws3, self.ws3_bytes = _workspace(need3.value if one_call else 0, dev, None)
         self._keep = (A, dY, W, m, v)
 
+    def _buffers(self):
+        return [self.sample_norms, self.ws1, self.ws2, self.ws3, *self.G_priv]
+
+    def _mark_stream(self, stream) -> None:
+        """Buffers allocated on the construction stream and used on another
+        one are marked as in use there, so that freeing this object does not
+        release them to other work before that stream reaches this point."""
+        if stream is not None and stream != torch.cuda.current_stream():
+            for t in self._buffers():
+                t.record_stream(stream)
+
     def run(self, step: int, stream=None) -> None:
         C, sigma, seed, lr, b1, b2, eps = self.hyper
         h = _stream_handle(stream)
         lib = self.lib
+        self._mark_stream(stream)
         if self.one_call:
             _check(lib, lib.dpg_private_step(
                 self.grads, self.params, self.n, self.B, self.T, self.r,
@@ -512,10 +550,14 @@ class PreparedStreamingStep(PreparedStep):
             h.d_out, h.layer_id = self.grads[i].d_out, self.grads[i].layer_id
             h.G_hat, h.G_priv = self.G_hat[i].data_ptr(), self.G_priv[i].data_ptr()
 
+    def _buffers(self):
+        return super()._buffers() + [self.norm_sq, self.wsl, self.wsc, *self.G_hat]
+
     def run(self, step: int, stream=None) -> None:
         C, sigma, seed, lr, b1, b2, eps = self.hyper
         h = _stream_handle(stream)
         lib = self.lib
+        self._mark_stream(stream)
         with torch.cuda.stream(stream) if stream is not None else _nullctx():
             self.norm_sq.zero_()
         for i in range(self.n):

@@ -110,17 +110,19 @@ size_t elem_size(int32_t dtype) { return dtype == DPG_BF16 ? 2 : 4; }
 
 bool valid_dtype(int32_t dtype) { return dtype == DPG_FP32 || dtype == DPG_BF16; }
 
-// Shape checks shared by both calls. Limits keep every kernel index in range:
-// r*d fits the 32-bit Philox element counter, tile counts fit int32.
+// Shape checks shared by every call. Limits keep every kernel index in range:
+// r*d_in and r*d_out below 2^31 fit the int32 element counts of the Adam
+// and final passes (and the 32-bit Philox element counter), and tile counts
+// fit int32.
+constexpr int64_t kMaxRD = (1ll << 31) - 8;
 int check_layer_shape(int64_t d_in, int64_t d_out, int32_t r, int idx) {
   const std::string at = " (layer index " + std::to_string(idx) + ")";
   if (d_in < 1 || d_out < 1)
     return fail(DPG_ERR_INVALID_ARG, "d_in and d_out must be >= 1" + at);
   if (d_in > (1 << 30) || d_out > (1 << 30))
     return fail(DPG_ERR_INVALID_ARG, "d_in and d_out must be <= 2^30" + at);
-  if (static_cast<uint64_t>(r) * d_in > kMaxU32 - 8 ||
-      static_cast<uint64_t>(r) * d_out > kMaxU32 - 8)
-    return fail(DPG_ERR_INVALID_ARG, "r*d_in and r*d_out must be < 2^32" + at);
+  if (static_cast<int64_t>(r) * d_in > kMaxRD || static_cast<int64_t>(r) * d_out > kMaxRD)
+    return fail(DPG_ERR_INVALID_ARG, "r*d_in and r*d_out must be < 2^31 - 8" + at);
   return DPG_OK;
 }
 
@@ -143,27 +145,7 @@ int check_unique_ids(const L* layers, int32_t n) {
 // run at (their register use allows two 256-thread blocks per CU).
 int64_t target_blocks(int32_t) { return 512; }
 
-#ifndef DPG_PROJ_BIG
-#define DPG_PROJ_BIG 1
-#endif
-constexpr bool kProjBig = DPG_PROJ_BIG != 0;
-
 int step_of(int32_t dtype) { return dtype == DPG_BF16 ? kStepBf16 : kStepF32; }
-
-#ifndef DPG_BACK_BIG
-#define DPG_BACK_BIG 1
-#endif
-constexpr bool kBackBig = DPG_BACK_BIG != 0;
-
-#ifndef DPG_HAT_SUM
-#define DPG_HAT_SUM 1
-#endif
-constexpr bool kHatSum = DPG_HAT_SUM != 0;
-
-#ifndef DPG_SAMP_BIG
-#define DPG_SAMP_BIG 1
-#endif
-constexpr bool kSampBig = DPG_SAMP_BIG != 0;
 
 // Tiling of the two per-sample passes (squared-norm partials, clipped sum).
 struct SampPlan {
@@ -241,7 +223,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // (written and read back) at the bytes one step moves per CU.
   // (its epilogue stores use 32-bit offsets: all of Xt, and 256 rows of a
   // split partial)
-  p.big = kProjBig && dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN &&
+  p.big = dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN &&
           static_cast<uint64_t>(B) * r * p.ldt * 2 < (1ull << 32) &&
           static_cast<uint64_t>(BT) * 4 * kBigM < (1ull << 32);
   for (int l = 0; l < n_layers; ++l)
@@ -372,7 +354,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // The norm run and the sum group minimise the same estimates, summed over
   // the launches, with the rounds of resident blocks counted in K steps
   // (plus two per block for the pipeline's fill).
-  p.has_samp_big = kSampBig && dtype == DPG_BF16 && r % kBigM == 0 && T % kSampBigK == 0;
+  p.has_samp_big = dtype == DPG_BF16 && r % kBigM == 0 && T % kSampBigK == 0;
   for (int l = 0; l < n_layers; ++l)  // (stored products: 32-bit offsets over 256 rows)
     if (layers[l].d_out % kBigN != 0 ||
         static_cast<uint64_t>(layers[l].d_out) * 4 * kBigM >= (1ull << 32))
@@ -421,7 +403,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     b.fuse_scale = b.per_group <= kFuseMaxGroup && b.n_slots <= kFuseMaxSlots;
   }
 
-  p.hat_sum = kHatSum && 8 * static_cast<int64_t>(r) <= T;
+  p.hat_sum = 8 * static_cast<int64_t>(r) <= T;
   const int32_t groups = std::max<int64_t>({static_cast<int64_t>(q.groups),
                                             p.has_samp_big ? p.samp_big.groups : 0,
                                             p.hat_sum ? B : 0});
@@ -546,7 +528,7 @@ int enqueue_back(const dpg_layer_param* params, int l0, int l1, int32_t r,
   // block per CU sweeps a run of column tiles, the run minimising (rounds of
   // resident blocks) x (tiles per block) x (K steps per tile plus about four
   // steps' worth of W traffic), ties to the longer run.
-  b.big = kBackBig && bf16 && r % kSampBigK == 0 && r > step_of(dtype);
+  b.big = bf16 && r % kSampBigK == 0 && r > step_of(dtype);
   for (int l = l0; l < l1; ++l)
     if (params[l].d_in % kBigM != 0 || params[l].d_out % kBigN != 0 ||
         !aligned(params[l].W, 16) || !aligned(P_of(l), 16) || !aligned(U_of(l), 16) ||
@@ -953,7 +935,36 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   return DPG_OK;
 }
 
+// Validates the one-call step's update arguments and runs it in `workspace`.
+int private_step_impl(const dpg_layer_grad* layers, const dpg_layer_param* params,
+                      int32_t n_layers, int64_t B, int64_t T, int32_t r, int32_t dtype,
+                      double clip_C, double sigma, double lr, double beta1, double beta2,
+                      double eps, uint64_t seed, uint64_t step, uint64_t proj_step,
+                      float* sample_norms, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!params) return fail(DPG_ERR_INVALID_ARG, "params is NULL");
+  int st = validate_adam_shapes(params, n_layers, r, dtype);
+  if (st) return st;
+  if (!layers) return fail(DPG_ERR_INVALID_ARG, "layers is NULL");
+  for (int i = 0; i < n_layers; ++i) {
+    if (params[i].d_in != layers[i].d_in || params[i].d_out != layers[i].d_out ||
+        params[i].layer_id != layers[i].layer_id)
+      return fail(DPG_ERR_INVALID_ARG, "params and layers differ at layer index " +
+                                           std::to_string(i));
+    if (!params[i].W || !params[i].m || !params[i].v)
+      return fail(DPG_ERR_INVALID_ARG,
+                  "NULL data pointer in layer index " + std::to_string(i));
+  }
+  if ((st = check_adam_hyper(lr, beta1, beta2, eps))) return st;
+  const StepUpdate upd{params, lr, beta1, beta2, eps};
+  return project_impl(layers, n_layers, B, T, r, dtype, clip_C, sigma, seed, step,
+                      proj_step, sample_norms, workspace, workspace_bytes, stream,
+                      nullptr, nullptr, &upd);
+}
+
 }  // namespace
+
+int dpg::record_error(int code, const char* msg) { return fail(code, msg); }
 
 extern "C" {
 
@@ -1024,24 +1035,9 @@ int dpg_private_step(const dpg_layer_grad* layers, const dpg_layer_param* params
                      uint64_t step, uint64_t proj_step, float* sample_norms,
                      void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (!params) return fail(DPG_ERR_INVALID_ARG, "params is NULL");
-  int st = validate_adam_shapes(params, n_layers, r, dtype);
-  if (st) return st;
-  if (!layers) return fail(DPG_ERR_INVALID_ARG, "layers is NULL");
-  for (int i = 0; i < n_layers; ++i) {
-    if (params[i].d_in != layers[i].d_in || params[i].d_out != layers[i].d_out ||
-        params[i].layer_id != layers[i].layer_id)
-      return fail(DPG_ERR_INVALID_ARG, "params and layers differ at layer index " +
-                                           std::to_string(i));
-    if (!params[i].W || !params[i].m || !params[i].v)
-      return fail(DPG_ERR_INVALID_ARG,
-                  "NULL data pointer in layer index " + std::to_string(i));
-  }
-  if ((st = check_adam_hyper(lr, beta1, beta2, eps))) return st;
-  const StepUpdate upd{params, lr, beta1, beta2, eps};
-  return project_impl(layers, n_layers, B, T, r, dtype, clip_C, sigma, seed, step,
-                      proj_step, sample_norms, workspace, workspace_bytes, stream,
-                      nullptr, nullptr, &upd);
+  return private_step_impl(layers, params, n_layers, B, T, r, dtype, clip_C, sigma, lr,
+                           beta1, beta2, eps, seed, step, proj_step, sample_norms,
+                           workspace, workspace_bytes, stream);
 }
 
 int dpg_project_layer_workspace_size(const dpg_layer_grad* layer, int64_t B,

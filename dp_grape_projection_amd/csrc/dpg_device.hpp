@@ -75,22 +75,78 @@ __device__ __forceinline__ float uniform_open01(uint32_t x) {
   return static_cast<float>(((x >> 9) << 1) | 1u) * 5.9604644775390625e-08f;
 }
 
-// Box-Muller on the pairs (w0, w1) and (w2, w3), with the hardware
-// transcendental instructions: v_log_f32 (base 2, so -2 ln u = -2 ln 2 *
-// log2 u), v_sqrt_f32, and v_sin_f32 / v_cos_f32, whose argument is in
-// turns, so the angle 2 pi u is passed as u exactly. u >= 2^-24 keeps the
-// logarithm away from denormals. Measured against the float64 definition
-// over 4 M pairs: at most 9e-7 absolute error (|z| <= 5.8), against 6e-7 for
-// the library's logf / sincospif, at about a quarter of the instructions.
+// Box-Muller is evaluated in float64 and each normal is rounded to fp32 once,
+// so a normal is within half an fp32 ulp (2.4e-7 for |z| < 8) plus about
+// 1e-11 of its exact value. (fp32 arithmetic alone cannot hold 1e-6 in the
+// tails: there an ulp of z is 4.8e-7.) On gfx950 float64 adds and
+// multiply-adds issue at the rate of non-packed fp32 ones.
+
+// ln u for u in (0, 1) (a normal double): u = m 2^e with m in [1/sqrt 2,
+// sqrt 2), and ln m = 2 atanh(s) with s = (m - 1) / (m + 1), |s| <= 0.1716,
+// from the odd series atanh(s) = s (1 + s^2/3 + s^4/5 + ...) cut after the
+// s^10/11 term (truncation below 5e-11 relative).
+__device__ __forceinline__ double ln_unit(double u) {
+  double m = __builtin_amdgcn_frexp_mant(u);  // [0.5, 1)
+  int e = __builtin_amdgcn_frexp_exp(u);
+  if (m < 0.70710678118654752) {
+    m *= 2.0;
+    e -= 1;
+  }
+  const double s = (m - 1.0) / (m + 1.0);
+  const double s2 = s * s;
+  double p = 1.0 / 11.0;
+  p = fma(p, s2, 1.0 / 9.0);
+  p = fma(p, s2, 1.0 / 7.0);
+  p = fma(p, s2, 1.0 / 5.0);
+  p = fma(p, s2, 1.0 / 3.0);
+  p = fma(p, s2, 1.0);
+  return fma(static_cast<double>(e), 0.69314718055994531, 2.0 * s * p);
+}
+
+// cos and sin of the angle 2 pi t for t in (0, 1) given in turns. Quadrant
+// reduction is exact: q = round(4 t), f = t - q / 4 in [-1/8, 1/8] (t has 24
+// significant bits), x = 2 pi f in [-pi/4, pi/4]. Taylor polynomials: sin
+// through x^11 (truncation below 7e-12), cos through x^12 (below 4e-13);
+// then the quadrant rotates (cos x, sin x) by q quarter turns.
+__device__ __forceinline__ void cossin_turns(double t, double& c, double& s) {
+  const double q = __builtin_rint(4.0 * t);
+  const double x = (t - 0.25 * q) * 6.2831853071795865;
+  const double x2 = x * x;
+  double ps = -1.0 / 39916800.0;                  // -1/11!
+  ps = fma(ps, x2, 1.0 / 362880.0);
+  ps = fma(ps, x2, -1.0 / 5040.0);
+  ps = fma(ps, x2, 1.0 / 120.0);
+  ps = fma(ps, x2, -1.0 / 6.0);
+  const double sx = fma(ps * x2, x, x);
+  double pc = 1.0 / 479001600.0;                  // 1/12!
+  pc = fma(pc, x2, -1.0 / 3628800.0);
+  pc = fma(pc, x2, 1.0 / 40320.0);
+  pc = fma(pc, x2, -1.0 / 720.0);
+  pc = fma(pc, x2, 1.0 / 24.0);
+  pc = fma(pc, x2, -0.5);
+  const double cx = fma(pc, x2, 1.0);
+  switch (static_cast<int>(q) & 3) {
+    case 0: c = cx; s = sx; break;
+    case 1: c = -sx; s = cx; break;
+    case 2: c = -cx; s = -sx; break;
+    default: c = sx; s = -cx; break;
+  }
+}
+
+// Box-Muller on the pairs (w0, w1) and (w2, w3): R = sqrt(-2 ln u(w0)),
+// z0 = R cos(2 pi u(w1)), z1 = R sin(2 pi u(w1)), and likewise for (w2, w3).
+// u >= 2^-24, so the logarithm never sees a denormal.
 __device__ __forceinline__ void box_muller4(const uint32_t w[4], float z[4]) {
-  constexpr float kMinus2Ln2 = -1.3862943611198906f;
-  const float r0 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(uniform_open01(w[0])));
-  const float r1 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(uniform_open01(w[2])));
-  const float t0 = uniform_open01(w[1]), t1 = uniform_open01(w[3]);
-  z[0] = r0 * __builtin_amdgcn_cosf(t0);
-  z[1] = r0 * __builtin_amdgcn_sinf(t0);
-  z[2] = r1 * __builtin_amdgcn_cosf(t1);
-  z[3] = r1 * __builtin_amdgcn_sinf(t1);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const double u = static_cast<double>(uniform_open01(w[2 * h]));
+    const double t = static_cast<double>(uniform_open01(w[2 * h + 1]));
+    const double R = __builtin_sqrt(-2.0 * ln_unit(u));
+    double c, s;
+    cossin_turns(t, c, s);
+    z[2 * h] = static_cast<float>(R * c);
+    z[2 * h + 1] = static_cast<float>(R * s);
+  }
 }
 
 struct StreamKey {

@@ -22,13 +22,7 @@ constexpr int kSumBatch = 8;
 // Large projections (bf16, r and B*T whole multiples of 256, d_in of 64):
 // 256 x 256 output tiles, K steps of 64, operands copied to LDS by direct
 // loads in two stages, 8 waves per block.
-#ifndef DPG_BIG_K
-#define DPG_BIG_K 64
-#endif
-#ifndef DPG_BIG_STAGES
-#define DPG_BIG_STAGES 2
-#endif
-constexpr int kBigM = 256, kBigN = 256, kBigK = DPG_BIG_K, kBigStages = DPG_BIG_STAGES;
+constexpr int kBigM = 256, kBigN = 256, kBigK = 64, kBigStages = 2;
 constexpr int kSampBigK = 64;  // K step (over t) of the large norm and sum kernel
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this
@@ -233,6 +227,10 @@ struct BackArgs {
                       // big, the run of column tiles of a block
   int32_t big;        // back_big_kernel: kBigM x kBigN tiles, steps of kSampBigK
 };
+
+// Records `msg` as the calling thread's last error (dpg_last_error) and
+// returns `code` (dpg_api.hip; for the library's other host sources).
+int record_error(int code, const char* msg);
 
 // Launchers (dpg_kernels.hip). Each returns the hipError_t of its launch.
 hipError_t launch_gen_p(const GenPArgs& a, int n_blocks, bool bf16_out,

@@ -115,7 +115,7 @@ int dpg_project_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
  * Arguments:
  *   layers, n_layers  host array of n_layers >= 1 layer descriptors
  *   B, T              batch size and tokens per sample (>= 1)
- *   r                 projection rank (>= 1); r*d_in and r*d_out < 2^32
+ *   r                 projection rank (>= 1); r*d_in and r*d_out <= 2^31 - 8
  *   dtype             DPG_FP32 or DPG_BF16 (element type of A and dY)
  *   clip_C            clip threshold C > 0, or +INFINITY for no clipping
  *   sigma             noise multiplier >= 0 and finite; must be 0 if C is inf

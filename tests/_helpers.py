@@ -6,12 +6,16 @@ import numpy as np
 
 import workloads as W
 
-# Parity bars (max relative Frobenius error per tensor per layer): fp32
-# inputs 1e-5, bf16 inputs 2e-2.
+# Parity bars: fp32 inputs 1e-5, bf16 inputs 2e-2, applied by rel_err to
+# every piece of a tensor (below), not to the tensor as a whole.
 TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+# Width of the row pieces rel_err compares.
+SEG = 256
 
 
 def rel_fro(got, want) -> float:
+    """Relative Frobenius error of a whole tensor (reported beside rel_err)."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     den = np.linalg.norm(want)
@@ -19,6 +23,48 @@ def rel_fro(got, want) -> float:
     if den == 0.0:
         return float(num)
     return float(num / den)
+
+
+def rel_err(got, want, width: int = SEG) -> float:
+    """The parity metric: the largest relative Frobenius error over the
+    pieces of a tensor. A matrix is cut into pieces of one row and at most
+    `width` consecutive columns; each element of a vector (per-sample norms)
+    is a piece of its own. A localised mistake (one wrong column of an
+    8192-wide layer, one wrong row, one sample) then shows at full size
+    instead of being averaged over the whole tensor. A piece whose reference
+    is all zeros contributes its absolute error."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    if want.ndim <= 1:
+        got, want = got.reshape(-1, 1), want.reshape(-1, 1)
+    else:
+        got, want = got.reshape(-1, want.shape[-1]), want.reshape(-1, want.shape[-1])
+    worst = 0.0
+    for c0 in range(0, want.shape[1], width):
+        w, g = want[:, c0:c0 + width], got[:, c0:c0 + width]
+        den = np.linalg.norm(w, axis=1)
+        num = np.linalg.norm(g - w, axis=1)
+        r = np.where(den > 0.0, num / np.where(den > 0.0, den, 1.0), num)
+        worst = max(worst, float(r.max()))
+    return worst
+
+
+def rel_err_dw(W_new, W_old, dW_want, width: int = SEG) -> float:
+    """rel_err of the weight update dW = W_new - W_old against dW_want, with
+    the one fp32 rounding of the stored weights taken out. W_new is
+    fl32(W_old + dW): it is off the exact sum by up to half an ulp of W_new,
+    which for |W| near 0.1 and |dW| near 1e-3 is already 1e-5 of dW, the
+    whole fp32 bar. Each element's error is reduced by that half ulp (never
+    below zero) before the pieces are measured, so the figure is the error of
+    the update itself, understated by at most half an ulp per element."""
+    Wn = np.asarray(W_new, np.float32)
+    got = Wn.astype(np.float64) - np.asarray(W_old, np.float64)
+    want = np.asarray(dW_want, np.float64)
+    half = 0.5 * np.spacing(np.abs(Wn)).astype(np.float64)
+    diff = got - want
+    return rel_err(want + np.sign(diff) * np.maximum(np.abs(diff) - half, 0.0),
+                   want, width)
 
 
 def to_device(wl, arr):

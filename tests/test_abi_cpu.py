@@ -73,6 +73,39 @@ def _params(shapes, ids=None, ptr=0x1000):
     return arr
 
 
+def test_abi_names_and_status_codes():
+    """The boundary as built: workspace queries named *_workspace_size that
+    return a status and write the size through a pointer, and positive status
+    codes (0 is success). The C header and the binding agree on both."""
+    text = open(HEADER).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"(DPG_[A-Z0-9_]+) = (\d+)", text))
+    assert codes == {"DPG_OK": 0, "DPG_ERR_INVALID_ARG": 1, "DPG_ERR_WORKSPACE": 2,
+                     "DPG_ERR_UNSUPPORTED": 3, "DPG_ERR_HIP": 4,
+                     "DPG_FP32": 0, "DPG_BF16": 1}
+    b = dpg.binding
+    assert (b.DPG_OK, b.DPG_ERR_INVALID_ARG, b.DPG_ERR_WORKSPACE,
+            b.DPG_ERR_UNSUPPORTED, b.DPG_ERR_HIP) == (0, 1, 2, 3, 4)
+    for name in ("dpg_project_workspace_size", "dpg_adam_workspace_size",
+                 "dpg_step_workspace_size", "dpg_project_layer_workspace_size",
+                 "dpg_clip_workspace_size"):
+        decl = re.search(r"int\s+" + name + r"\s*\(([^)]*)\)", text, re.S)
+        assert decl and "size_t* bytes" in decl.group(1), name
+
+
+def test_r_times_d_limit_in_size_queries(lib):
+    """r*d_out = 2^31 is rejected by the workspace queries too."""
+    out = ctypes.c_size_t(0)
+    st = lib.dpg_project_workspace_size(_grads([(4, 2 ** 22)]), 1, 1, 1, 512, 1,
+                                        ctypes.byref(out))
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG
+    st = lib.dpg_adam_workspace_size(_params([(4, 2 ** 22)]), 1, 512, 1,
+                                     ctypes.byref(out))
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG
+    st = lib.dpg_project_workspace_size(_grads([(4, 2 ** 22 - 1)]), 1, 1, 1, 512, 1,
+                                        ctypes.byref(out))
+    assert st == 0
+
+
 def test_status_strings(lib):
     for code in range(5):
         assert lib.dpg_status_string(code).startswith(b"DPG_")
@@ -112,6 +145,9 @@ BAD_PROJECT = [
     ("duplicate ids", dict(ids=[3, 3])),
     ("zero d_in", dict(shapes=[(0, 4), (4, 4)])),
     ("huge r*d", dict(shapes=[(2 ** 30, 4), (4, 4)], r=8)),
+    # r*d_out = 2^31: the element counts of the final and Adam passes are int32
+    ("r*d_out 2^31", dict(shapes=[(4, 2 ** 22), (4, 4)], r=512)),
+    ("r*d_in 2^31", dict(shapes=[(2 ** 22, 4), (4, 4)], r=512)),
     ("null data", dict(ptr=0)),
 ]
 

@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import workloads as W
-from _helpers import TOL, make_case, rel_fro, to_device, torch_dtype
+from _helpers import TOL, make_case, rel_err, rel_err_dw, to_device, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -107,8 +107,8 @@ def test_one_call_step(name):
         # G_priv and norms against the oracle
         want = oracle.project_clip_noise(orc, wl.r, wl.clip_C, wl.sigma, wl.seed,
                                          step, 1)
-        e_n = rel_fro(n1.cpu().numpy(), want["norms"])
-        e_g = max(rel_fro(g, w) for g, w in zip(_np(G1), want["G_priv"]))
+        e_n = rel_err(n1.cpu().numpy(), want["norms"])
+        e_g = max(rel_err(g, w) for g, w in zip(_np(G1), want["G_priv"]))
         # the update, stage-isolated on the GPU's G_priv
         params = [{"W": c[0], "m": c[1], "v": c[2],
                    "G_priv": g.astype(np.float64), "layer_id": L.layer_id}
@@ -116,10 +116,10 @@ def test_one_call_step(name):
         upd = oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2,
                                       wl.eps, wl.seed, step, 1)
         Wn, mn, vn = _np(W1), _np(m1), _np(v1)
-        e_w = max(rel_fro(w.astype(np.float64) - c[0], u["dW"])
+        e_w = max(rel_err_dw(w, c[0], u["dW"])
                   for w, c, u in zip(Wn, cur, upd))
-        e_m = max(rel_fro(m, u["m"]) for m, u in zip(mn, upd))
-        e_v = max(rel_fro(v, u["v"]) for v, u in zip(vn, upd))
+        e_m = max(rel_err(m, u["m"]) for m, u in zip(mn, upd))
+        e_v = max(rel_err(v, u["v"]) for v, u in zip(vn, upd))
         print(f"[one-call] {name} step {step}: norms {e_n:.2e} G_priv {e_g:.2e} "
               f"dW {e_w:.2e} m {e_m:.2e} v {e_v:.2e}", flush=True)
         assert max(e_n, e_g, e_w, e_m, e_v) <= tol
@@ -205,12 +205,12 @@ def test_unaligned_caller_tensors(name):
     upd = oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2, wl.eps,
                                   wl.seed, 1, 1)
     for G, n, Ws, ms, vs in ((G1, n1, W1, m1, v1), (G2, n2, W2, m2, v2)):
-        e_n = rel_fro(n.cpu().numpy(), want["norms"])
-        e_g = max(rel_fro(g, w) for g, w in zip(_np(G), want["G_priv"]))
-        e_w = max(rel_fro(w.astype(np.float64) - s[0], u["dW"])
+        e_n = rel_err(n.cpu().numpy(), want["norms"])
+        e_g = max(rel_err(g, w) for g, w in zip(_np(G), want["G_priv"]))
+        e_w = max(rel_err_dw(w, s[0], u["dW"])
                   for w, s, u in zip(_np(Ws), state, upd))
-        e_m = max(rel_fro(m, u["m"]) for m, u in zip(_np(ms), upd))
-        e_v = max(rel_fro(v, u["v"]) for v, u in zip(_np(vs), upd))
+        e_m = max(rel_err(m, u["m"]) for m, u in zip(_np(ms), upd))
+        e_v = max(rel_err(v, u["v"]) for v, u in zip(_np(vs), upd))
         print(f"[unaligned] {name}: norms {e_n:.2e} G_priv {e_g:.2e} dW {e_w:.2e} "
               f"m {e_m:.2e} v {e_v:.2e}", flush=True)
         assert max(e_n, e_g, e_w, e_m, e_v) <= tol
@@ -218,3 +218,39 @@ def test_unaligned_caller_tensors(name):
     assert torch.equal(n1, n2)
     for a, b in zip(G1 + W1 + m1 + v1, G2 + W2 + m2 + v2):
         assert torch.equal(a, b)
+
+
+def test_side_stream_matches_default_stream():
+    """A call given a stream other than torch's current one: its outputs and
+    temporary workspace are allocated for that stream, and the results equal
+    the default-stream call's bit for bit."""
+    import torch
+    import dp_grape_projection_amd as dpg
+    wl = CASES["ragged_bf16"]
+    host, _, state = make_case(wl)
+    A = [to_device(wl, a) for a, _ in host]
+    dY = [to_device(wl, d) for _, d in host]
+    ids = [L.layer_id for L in wl.layers]
+    kw = dict(r=wl.r, clip_C=wl.clip_C, sigma=wl.sigma, seed=wl.seed,
+              step=wl.step, proj_step=wl.proj_step, layer_ids=ids)
+    G0, n0 = dpg.dpg_project_clip_noise(A, dY, **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    G1, n1 = dpg.dpg_project_clip_noise(A, dY, stream=side, **kw)
+    Wd, md, vd = _state(state)
+    Wd2, md2, vd2 = _state(state)
+    dpg.dpg_adam_backproject(G0, Wd, md, vd, wl.r, wl.lr, wl.beta1, wl.beta2,
+                             wl.eps, wl.seed, wl.step, wl.proj_step,
+                             layer_ids=ids, dtype=torch_dtype(wl))
+    side.wait_stream(torch.cuda.current_stream())
+    dpg.dpg_adam_backproject(G1, Wd2, md2, vd2, wl.r, wl.lr, wl.beta1, wl.beta2,
+                             wl.eps, wl.seed, wl.step, wl.proj_step,
+                             layer_ids=ids, dtype=torch_dtype(wl), stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(n0, n1)
+    for a, b in zip(G0, G1):
+        assert torch.equal(a, b)
+    for x, y in zip(Wd + md + vd, Wd2 + md2 + vd2):
+        assert torch.equal(x, y)

@@ -1,8 +1,10 @@
 """GPU parity: libdpg (through its C ABI) against the float64 CPU oracle.
 
 Each case feeds the same seeded inputs to both sides and compares, per layer
-and per tensor, the relative Frobenius error against the bar for the input
-type (fp32 1e-5, bf16 2e-2):
+and per tensor, the largest relative Frobenius error over the pieces of the
+tensor (one row cut into runs of 256 columns; each sample's norm on its own;
+tests/_helpers.rel_err) against the bar for the input type (fp32 1e-5, bf16
+2e-2):
   * sample norms n_i and the privatised projected gradient G_priv, with the
     workload's sigma and with sigma = 0 (with noise on, G_priv is dominated
     by the noise, so sigma = 0 is what checks the contraction);
@@ -20,7 +22,7 @@ import pytest
 
 import oracle
 import workloads as W
-from _helpers import (TOL, make_case, rel_fro, run_adam, run_project,
+from _helpers import (TOL, make_case, rel_err, rel_err_dw, run_adam, run_project,
                       to_device, torch_dtype)
 
 pytestmark = pytest.mark.gpu
@@ -44,19 +46,29 @@ def gpu_and_library():
     (0, 5, 1, 1, 3, 1001),
     (2 ** 40 + 7, 143, 99, 0, 12345, 777),
     (123456789, 7, 2 ** 32 - 1, 1, 2 ** 31, 64),
+    # 2^23 values reach the tails: six with |z| > 5, max |z| = 5.47
+    (0, 3, 1, 0, 0, 1 << 23),
 ])
 def test_philox_stream(seed, layer, stepw, tag, start, n):
+    """Philox words bit for bit; normals within 1e-6 absolute of the float64
+    definition and, more tightly, within half an fp32 ulp (the kernels
+    evaluate Box-Muller in float64 and round once) plus 1e-10."""
     import dp_grape_projection_amd as dpg
     from oracle.philox import philox_words
     z, w = dpg.dpg_philox_normals(seed, layer, stepw, tag, start, n, words=True)
-    z = z.cpu().numpy().astype(np.float64)
+    z32 = z.cpu().numpy()
+    z = z32.astype(np.float64)
     w = w.cpu().numpy().view(np.uint32).reshape(-1, 4)
     c = np.arange(start >> 2, ((start + n - 1) >> 2) + 1, dtype=np.uint64)
     want_w = np.stack(philox_words(seed, layer, stepw, tag, c), axis=1)
     np.testing.assert_array_equal(w, want_w)
     want_z = oracle.gaussian_stream(seed, layer, stepw, tag, n, start=start)
     err = np.abs(z - want_z)
-    assert err.max() <= 4e-6 * max(1.0, np.abs(want_z).max()), err.max()
+    print(f"[philox] n={n}: max |z| {np.abs(want_z).max():.3f}, "
+          f"max abs error {err.max():.3e}", flush=True)
+    assert err.max() <= 1e-6, err.max()
+    half_ulp = 0.5 * np.spacing(np.abs(z32)).astype(np.float64)
+    assert np.all(err <= half_ulp + 1e-10), (err - half_ulp).max()
 
 
 # --------------------------------------------------------------- the step --
@@ -166,9 +178,9 @@ def _check_project(wl, host, orc, sigma, C=None, tag=""):
     want = oracle.project_clip_noise(orc, wl.r, C, sigma, wl.seed, wl.step,
                                      wl.proj_step)
     tol = TOL[wl.dtype]
-    e_n = rel_fro(n, want["norms"])
+    e_n = rel_err(n, want["norms"])
     assert e_n <= tol, f"{tag} norms {e_n}"
-    errs = [rel_fro(g, w) for g, w in zip(G, want["G_priv"])]
+    errs = [rel_err(g, w) for g, w in zip(G, want["G_priv"])]
     print(f"[{wl.name}{tag} sigma={sigma}] norms {e_n:.2e} "
           f"G_priv max {max(errs):.2e}", flush=True)
     assert max(errs) <= tol, errs
@@ -186,8 +198,8 @@ def _check_adam(wl, G, state, tag=""):
     tol = TOL[wl.dtype]
     worst = 0.0
     for (Wn, mn, vn), s, w in zip(new, state, want):
-        dW = Wn.astype(np.float64) - s[0].astype(np.float64)
-        e = max(rel_fro(dW, w["dW"]), rel_fro(mn, w["m"]), rel_fro(vn, w["v"]))
+        e = max(rel_err_dw(Wn, s[0], w["dW"]), rel_err(mn, w["m"]),
+                rel_err(vn, w["v"]))
         worst = max(worst, e)
     print(f"[{wl.name}{tag}] adam+backproject (stage-isolated) {worst:.2e}",
           flush=True)
@@ -220,10 +232,9 @@ def test_tiny_end_to_end_fp32():
     w2 = oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2,
                                  wl.eps, wl.seed, wl.step, wl.proj_step)
     for (Wn, mn, vn), s, w in zip(new, state, w2):
-        dW = Wn.astype(np.float64) - s[0].astype(np.float64)
-        assert rel_fro(dW, w["dW"]) <= TOL["fp32"]
-        assert rel_fro(mn, w["m"]) <= TOL["fp32"]
-        assert rel_fro(vn, w["v"]) <= TOL["fp32"]
+        assert rel_err_dw(Wn, s[0], w["dW"]) <= TOL["fp32"]
+        assert rel_err(mn, w["m"]) <= TOL["fp32"]
+        assert rel_err(vn, w["v"]) <= TOL["fp32"]
 
 
 def test_noise_alone_matches_stream():
@@ -235,7 +246,7 @@ def test_noise_alone_matches_stream():
     assert np.all(n == 0.0)
     for g, L in zip(G, wl.layers):
         Z = oracle.noise_matrix(wl.seed, L.layer_id, wl.step, wl.r, L.d_out)
-        assert rel_fro(g, wl.sigma * wl.clip_C * Z / wl.B) <= 1e-6
+        assert rel_err(g, wl.sigma * wl.clip_C * Z / wl.B) <= 1e-6
 
 
 def test_no_clipping_is_plain_mean():
@@ -247,7 +258,7 @@ def test_no_clipping_is_plain_mean():
     want = oracle.project_clip_noise(orc, wl.r, math.inf, 0.0, wl.seed,
                                      wl.step, wl.proj_step)
     for g, w in zip(G, want["G_priv"]):
-        assert rel_fro(g, w) <= TOL["bf16"]
+        assert rel_err(g, w) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "groups_bf16", "groups_fp32",
@@ -308,8 +319,8 @@ def test_three_steps_and_resume():
         want = oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2,
                                        wl.eps, wl.seed, step, step)
         for (Wn, mn, vn), c, w in zip(new, cur, want):
-            assert rel_fro(Wn.astype(np.float64) - c[0], w["dW"]) <= TOL["bf16"]
-            assert rel_fro(mn, w["m"]) <= TOL["bf16"]
+            assert rel_err_dw(Wn, c[0], w["dW"]) <= TOL["bf16"]
+            assert rel_err(mn, w["m"]) <= TOL["bf16"]
         cur = new
     torch.cuda.synchronize()
     for (Wn, mn, vn), w, m, v in zip(cur, Wd, md, vd):
@@ -335,6 +346,6 @@ def test_mlp4_full_size():
               for s, g, L in zip(state, want["G_priv"], wl.layers)]
     w2 = oracle.adam_backproject(params, wl.r, wl.lr, wl.beta1, wl.beta2,
                                  wl.eps, wl.seed, wl.step, wl.proj_step)
-    e2e = max(rel_fro(n[0].astype(np.float64) - s[0], w["dW"])
+    e2e = max(rel_err_dw(n[0], s[0], w["dW"])
               for n, s, w in zip(new, state, w2))
     print(f"[mlp4] end-to-end dW rel error (reported) {e2e:.3e}", flush=True)

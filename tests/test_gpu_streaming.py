@@ -20,7 +20,7 @@ import pytest
 
 import oracle
 import workloads as W
-from _helpers import TOL, make_case, rel_fro, to_device
+from _helpers import TOL, make_case, rel_err, rel_err_dw, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -85,16 +85,16 @@ def test_streaming_parity(name):
                                      lay["A"].shape[2])
         want = np.stack([P @ oracle.per_sample_gradient(lay["A"][i], lay["dY"][i])
                          for i in range(wl.B)])
-        worst = max(worst, rel_fro(g, want))
+        worst = max(worst, rel_err(g, want))
     want = oracle.project_clip_noise(orc, wl.r, wl.clip_C, 0.0, wl.seed, wl.step,
                                      wl.proj_step)
-    e_sq = rel_fro(nsq, want["norms"] ** 2)
-    e_n = rel_fro(n, want["norms"])
-    e_g0 = max(rel_fro(g, w) for g, w in zip(G0, want["G_priv"]))
+    e_sq = rel_err(nsq, want["norms"] ** 2)
+    e_n = rel_err(n, want["norms"])
+    e_g0 = max(rel_err(g, w) for g, w in zip(G0, want["G_priv"]))
     _, _, G1, _ = _stream(wl, host, wl.sigma)
     want1 = oracle.project_clip_noise(orc, wl.r, wl.clip_C, wl.sigma, wl.seed,
                                       wl.step, wl.proj_step)
-    e_g1 = max(rel_fro(g, w) for g, w in zip(G1, want1["G_priv"]))
+    e_g1 = max(rel_err(g, w) for g, w in zip(G1, want1["G_priv"]))
     print(f"[stream] {name}: G_hat {worst:.2e} norm_sq {e_sq:.2e} norms {e_n:.2e} "
           f"G_priv sigma=0 {e_g0:.2e} sigma={wl.sigma} {e_g1:.2e}", flush=True)
     assert max(worst, e_sq, e_n, e_g0, e_g1) <= tol
@@ -104,8 +104,8 @@ def test_streaming_parity(name):
     Gf, nf = dpg.dpg_project_clip_noise(A, dY, wl.r, wl.clip_C, 0.0, wl.seed, wl.step,
                                         wl.proj_step,
                                         layer_ids=[L.layer_id for L in wl.layers])
-    e_f = max(rel_fro(g, f.cpu().numpy()) for g, f in zip(G0, Gf))
-    assert e_f <= tol and rel_fro(n, nf.cpu().numpy()) <= tol
+    e_f = max(rel_err(g, f.cpu().numpy()) for g, f in zip(G0, Gf))
+    assert e_f <= tol and rel_err(n, nf.cpu().numpy()) <= tol
 
 
 def test_streaming_mixed_clipping_and_no_clipping():
@@ -118,7 +118,7 @@ def test_streaming_mixed_clipping_and_no_clipping():
         _, _, G, n = _stream(wl, host, 0.0, C=c)
         want = oracle.project_clip_noise(orc, wl.r, c, 0.0, wl.seed, wl.step,
                                          wl.proj_step)
-        assert max(rel_fro(g, w) for g, w in zip(G, want["G_priv"])) <= TOL["bf16"]
+        assert max(rel_err(g, w) for g, w in zip(G, want["G_priv"])) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -155,17 +155,17 @@ def test_autograd_driver_two_steps(dtype):
                    "dY": opt.inputs[i][1].float().cpu().numpy().astype(np.float64),
                    "layer_id": i} for i in (3, 8)]
         want = oracle.project_clip_noise(layers, r, C, sigma, seed, step, step)
-        e_n = rel_fro(opt.last_norms.cpu().numpy(), want["norms"])
-        e_g = max(rel_fro(g.cpu().numpy(), w)
+        e_n = rel_err(opt.last_norms.cpu().numpy(), want["norms"])
+        e_g = max(rel_err(g.cpu().numpy(), w)
                   for g, w in zip(opt.last_G_priv, want["G_priv"]))
         # the update, stage-isolated on the GPU's G_priv
         params = [{"W": W_old[i], "m": m[i], "v": v[i],
                    "G_priv": g.cpu().numpy().astype(np.float64), "layer_id": i}
                   for i, g in zip((3, 8), opt.last_G_priv)]
         upd = oracle.adam_backproject(params, r, lr, 0.9, 0.999, 1e-8, seed, step, step)
-        e_w = max(rel_fro(lw.W.cpu().numpy().astype(np.float64) - W_old[i], u["dW"])
+        e_w = max(rel_err_dw(lw.W.cpu().numpy(), W_old[i], u["dW"])
                   for lw, i, u in zip((l0, l1), (3, 8), upd))
-        e_m = max(rel_fro(mm.cpu().numpy(), u["m"]) for mm, u in zip(opt.m, upd))
+        e_m = max(rel_err(mm.cpu().numpy(), u["m"]) for mm, u in zip(opt.m, upd))
         print(f"[autograd {dtype}] step {step}: norms {e_n:.2e} G_priv {e_g:.2e} "
               f"dW {e_w:.2e} m {e_m:.2e}", flush=True)
         assert max(e_n, e_g, e_w, e_m) <= tol
