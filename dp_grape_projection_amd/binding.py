@@ -33,7 +33,8 @@ EXPORTED = (
     "dpg_adam_workspace_size", "dpg_adam_backproject", "dpg_philox_normals",
     "dpg_project_layer_workspace_size", "dpg_project_layer",
     "dpg_clip_workspace_size", "dpg_clip_sum_noise",
-    "dpg_step_workspace_size", "dpg_private_step",
+    "dpg_step_workspace_size", "dpg_private_step", "dpg_private_step_static",
+    "dpg_static_scratch_bytes",
     "dpg_status_string", "dpg_last_error", "dpg_version",
     "dpg_timing_enable", "dpg_timing_read", "dpg_kernel_name",
 )
@@ -108,11 +109,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dpg_private_step.argtypes = [
         ctypes.POINTER(LayerGrad), ctypes.POINTER(LayerParam), i32, i64, i64, i32,
         i32, f64, f64, f64, f64, f64, f64, u64, u64, u64, vp, vp, sz, vp]
+    lib.dpg_private_step_static.argtypes = [
+        ctypes.POINTER(LayerGrad), ctypes.POINTER(LayerParam), i32, i64, i64, i32,
+        i32, f64, f64, f64, f64, f64, f64, u64, u64, u64, vp, vp]
+    lib.dpg_static_scratch_bytes.argtypes = []
     lib.dpg_clip_sum_noise.argtypes = [
         ctypes.POINTER(LayerHat), i32, i64, i32, f64, f64, u64, u64, vp, vp, vp,
         sz, vp]
     for name in EXPORTED:
         getattr(lib, name).restype = ctypes.c_int
+    lib.dpg_static_scratch_bytes.restype = ctypes.c_size_t
     lib.dpg_status_string.restype = ctypes.c_char_p
     lib.dpg_status_string.argtypes = [ctypes.c_int]
     lib.dpg_last_error.restype = ctypes.c_char_p
@@ -331,6 +337,64 @@ def dpg_private_step(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
     return ps.G_priv, ps.sample_norms
 
 
+def static_scratch_bytes() -> int:
+    """Bytes of the library's static scratch (per GPU)."""
+    return int(load_library().dpg_static_scratch_bytes())
+
+
+@_on_stream
+def dpg_private_step_static(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
+                            W: Sequence[torch.Tensor], m: Sequence[torch.Tensor],
+                            v: Sequence[torch.Tensor], G_priv: Sequence[torch.Tensor],
+                            sample_norms: torch.Tensor, r: int, clip_C: float,
+                            sigma: float, lr: float, beta1: float, beta2: float,
+                            eps: float, seed: int, step: int,
+                            proj_step: Optional[int] = None,
+                            layer_ids: Optional[Sequence[int]] = None, stream=None):
+    """The one-call step in the library's static scratch (libdpg
+    dpg_private_step_static): nothing is allocated, here or in the library;
+    the caller passes every output (G_priv [r, d_out] fp32 per layer,
+    sample_norms [B] fp32). W, m, v are updated in place."""
+    lib = load_library()
+    grads, params, n, B, T, code = _step_tables(A, dY, W, m, v, G_priv, r, layer_ids)
+    _require(sample_norms, "sample_norms", torch.float32, (B,))
+    proj_step = step if proj_step is None else proj_step
+    _check(lib, lib.dpg_private_step_static(
+        grads, params, n, B, T, int(r), code, float(clip_C), float(sigma), float(lr),
+        float(beta1), float(beta2), float(eps), int(seed), int(step), int(proj_step),
+        sample_norms.data_ptr(), _stream_handle(stream)))
+    return G_priv, sample_norms
+
+
+def _step_tables(A, dY, W, m, v, G_priv, r, layer_ids):
+    """Checked layer tables (dpg_layer_grad, dpg_layer_param) of one step."""
+    n = len(A)
+    if n < 1 or not (len(dY) == len(W) == len(m) == len(v) == len(G_priv) == n):
+        raise ValueError("A, dY, W, m, v and G_priv must be lists of equal length >= 1")
+    dt = A[0].dtype
+    B, T = int(A[0].shape[0]), int(A[0].shape[1])
+    ids = list(range(n)) if layer_ids is None else [int(x) for x in layer_ids]
+    grads, params = (LayerGrad * n)(), (LayerParam * n)()
+    for i in range(n):
+        _require(A[i], f"A[{i}]", dt)
+        _require(dY[i], f"dY[{i}]", dt)
+        if A[i].dim() != 3 or dY[i].dim() != 3 or \
+                tuple(A[i].shape[:2]) != (B, T) or tuple(dY[i].shape[:2]) != (B, T):
+            raise ValueError(f"layer {i}: A and dY must be [B, T, d] with common B, T")
+        d_in, d_out = int(A[i].shape[2]), int(dY[i].shape[2])
+        _require(W[i], f"W[{i}]", torch.float32, (d_in, d_out))
+        for name, t in (("G_priv", G_priv[i]), ("m", m[i]), ("v", v[i])):
+            _require(t, f"{name}[{i}]", torch.float32, (r, d_out))
+        g, p = grads[i], params[i]
+        g.d_in = p.d_in = d_in
+        g.d_out = p.d_out = d_out
+        g.layer_id = p.layer_id = ids[i]
+        g.A, g.dY, g.G_priv = A[i].data_ptr(), dY[i].data_ptr(), G_priv[i].data_ptr()
+        p.G_priv, p.W = G_priv[i].data_ptr(), W[i].data_ptr()
+        p.m, p.v = m[i].data_ptr(), v[i].data_ptr()
+    return grads, params, n, B, T, _dtype_code(dt)
+
+
 @_on_stream
 def dpg_project_layer(A: torch.Tensor, dY: torch.Tensor, r: int, seed: int,
                       proj_step: int, layer_id: int, norm_sq: torch.Tensor,
@@ -448,23 +512,8 @@ class PreparedStep:
                                  for d in dY]
         self.sample_norms = (torch.empty(self.B, dtype=torch.float32, device=dev)
                              if sample_norms is None else sample_norms)
-        self.grads = (LayerGrad * n)()
-        self.params = (LayerParam * n)()
-        for i in range(n):
-            _require(A[i], f"A[{i}]", dt)
-            _require(dY[i], f"dY[{i}]", dt)
-            d_in, d_out = int(A[i].shape[2]), int(dY[i].shape[2])
-            _require(W[i], f"W[{i}]", torch.float32, (d_in, d_out))
-            for name, t in (("G_priv", self.G_priv[i]), ("m", m[i]), ("v", v[i])):
-                _require(t, f"{name}[{i}]", torch.float32, (r, d_out))
-            g, p = self.grads[i], self.params[i]
-            g.d_in = p.d_in = d_in
-            g.d_out = p.d_out = d_out
-            g.layer_id = p.layer_id = ids[i]
-            g.A, g.dY, g.G_priv = A[i].data_ptr(), dY[i].data_ptr(), \
-                self.G_priv[i].data_ptr()
-            p.G_priv, p.W = self.G_priv[i].data_ptr(), W[i].data_ptr()
-            p.m, p.v = m[i].data_ptr(), v[i].data_ptr()
+        self.grads, self.params, _, _, _, _ = _step_tables(A, dY, W, m, v, self.G_priv,
+                                                           r, ids)
         self.n = n
         self.r = int(r)
         self.hyper = (float(clip_C), float(sigma), int(seed), float(lr),

@@ -189,6 +189,29 @@ int dpg_private_step(const dpg_layer_grad* layers, const dpg_layer_param* params
                      uint64_t step, uint64_t proj_step, float* sample_norms,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * dpg_private_step_static: dpg_private_step without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * step's scratch is a static array of dpg_static_scratch_bytes() (64 MiB)
+ * that the library holds on each GPU it runs on until the process ends;
+ * the call itself allocates nothing. The caller still passes every input
+ * and output, with the arguments and results of dpg_private_step.
+ * Errors: a step whose scratch (dpg_step_workspace_size) exceeds the static
+ * array returns DPG_ERR_WORKSPACE before anything is enqueued. All calls on
+ * one GPU share that GPU's array, and it keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap in time on one
+ * GPU, from two host threads or on two streams with no ordering between
+ * them, race on it.
+ */
+size_t dpg_static_scratch_bytes(void);
+int dpg_private_step_static(const dpg_layer_grad* layers,
+                            const dpg_layer_param* params, int32_t n_layers,
+                            int64_t B, int64_t T, int32_t r, int32_t dtype,
+                            double clip_C, double sigma, double lr, double beta1,
+                            double beta2, double eps, uint64_t seed, uint64_t step,
+                            uint64_t proj_step, float* sample_norms, void* stream);
+
 /* ------------------------------------------------------------------------
  * Streaming form (Methodology, closing paragraph: the per-sample gradients
  * are projected layer by layer during the backward pass; the projected

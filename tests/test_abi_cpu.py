@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
               "dpg_philox_normals", "dpg_status_string", "dpg_last_error",
               "dpg_version", "dpg_project_layer", "dpg_clip_sum_noise",
               "dpg_project_layer_workspace_size", "dpg_clip_workspace_size",
-              "dpg_step_workspace_size", "dpg_private_step"):
+              "dpg_step_workspace_size", "dpg_private_step",
+              "dpg_private_step_static", "dpg_static_scratch_bytes"):
         assert n in names
     assert sorted(dpg.EXPORTED) == names
 
@@ -336,3 +337,22 @@ def test_private_step_workspace(lib):
     assert lib.dpg_private_step(*args, 0x10000, need.value - 1, None) == 2
     assert lib.dpg_private_step(*args, 0x10010, need.value, None) == 2
     assert b"workspace" in lib.dpg_last_error()
+
+
+def test_static_step_rejects_a_step_beyond_its_scratch(lib):
+    """dpg_private_step_static: a step whose scratch exceeds the static array
+    (enc12 needs about 1 GiB) fails with DPG_ERR_WORKSPACE before any HIP
+    call; so does an invalid shape, with DPG_ERR_INVALID_ARG."""
+    import workloads as W
+    assert lib.dpg_static_scratch_bytes() == 64 << 20
+    wl = W.workload("enc12")
+    shapes = [(L.d_in, L.d_out) for L in wl.layers]
+    ids = [L.layer_id for L in wl.layers]
+    n = len(shapes)
+    args = (_grads(shapes, ids), _params(shapes, ids), n, wl.B, wl.T, wl.r, 1,
+            1.0, 0.5, 1e-3, 0.9, 0.999, 1e-8, 0, 1, 1, None, None)
+    assert lib.dpg_private_step_static(*args) == dpg.binding.DPG_ERR_WORKSPACE
+    assert b"static scratch" in lib.dpg_last_error()
+    bad = list(args)
+    bad[5] = 0   # r = 0
+    assert lib.dpg_private_step_static(*bad) == dpg.binding.DPG_ERR_INVALID_ARG
