@@ -27,12 +27,15 @@ def rel_fro(got, want) -> float:
 
 def rel_err(got, want, width: int = SEG) -> float:
     """The parity metric: the largest relative Frobenius error over the
-    pieces of a tensor. A matrix is cut into pieces of one row and at most
-    `width` consecutive columns; each element of a vector (per-sample norms)
-    is a piece of its own. A localised mistake (one wrong column of an
-    8192-wide layer, one wrong row, one sample) then shows at full size
-    instead of being averaged over the whole tensor. A piece whose reference
-    is all zeros contributes its absolute error."""
+    pieces of a tensor. A matrix is cut into pieces of one row and `width`
+    consecutive columns (the last piece of a row is its last `width`
+    columns, overlapping the one before, so that no piece is a short tail
+    whose few elements make the ratio noisy; rows narrower than `width` are
+    one piece); each element of a vector (per-sample norms) is a piece of
+    its own. A localised mistake (one wrong column of an 8192-wide layer,
+    one wrong row, one sample) then shows at full size instead of being
+    averaged over the whole tensor. A piece whose reference is all zeros
+    contributes its absolute error."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
@@ -41,7 +44,9 @@ def rel_err(got, want, width: int = SEG) -> float:
     else:
         got, want = got.reshape(-1, want.shape[-1]), want.reshape(-1, want.shape[-1])
     worst = 0.0
-    for c0 in range(0, want.shape[1], width):
+    n = want.shape[1]
+    for c0 in range(0, n, width):
+        c0 = min(c0, max(n - width, 0))
         w, g = want[:, c0:c0 + width], got[:, c0:c0 + width]
         den = np.linalg.norm(w, axis=1)
         num = np.linalg.norm(g - w, axis=1)

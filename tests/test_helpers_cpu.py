@@ -34,15 +34,19 @@ def test_uniform_noise_is_measured_like_the_tensor_metric():
     assert a <= b <= 2.0 * a
 
 
-def test_ragged_pieces_and_zero_reference():
+def test_last_piece_and_zero_reference():
     want = np.zeros((3, 300))
     got = np.zeros((3, 300))
     got[2, 299] = 1e-7
     assert rel_err(got, want) == 1e-7      # absolute where the reference is 0
     want[:, :] = 1.0
     got = want.copy()
-    got[1, 260] = 1.1                        # in the 44-column tail piece
-    assert abs(rel_err(got, want) - 0.1 / np.sqrt(44)) < 1e-12
+    got[1, 260] = 1.1                        # in the last piece: columns 44..299
+    assert abs(rel_err(got, want) - 0.1 / np.sqrt(256)) < 1e-12
+    narrow = np.ones((2, 40))
+    bad = narrow.copy()
+    bad[0, 3] = 2.0                          # a row narrower than a piece
+    assert abs(rel_err(bad, narrow) - 1.0 / np.sqrt(40)) < 1e-12
 
 
 def test_dw_metric_takes_out_only_the_storage_rounding():
