@@ -22,7 +22,7 @@ constexpr int kSumBatch = 8;
 // Large projections (bf16, r and B*T whole multiples of 256, d_in of 64):
 // 256 x 256 output tiles, K steps of 64, operands copied to LDS by direct
 // loads in two stages, 8 waves per block.
-constexpr int kBigM = 256, kBigN = 256, kBigK = 64, kBigStages = 2;
+constexpr int kBigM = 256, kBigN = 256, kBigK = 64;
 constexpr int kSampBigK = 64;  // K step (over t) of the large norm and sum kernel
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this

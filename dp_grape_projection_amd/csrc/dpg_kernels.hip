@@ -291,15 +291,27 @@ __device__ __forceinline__ void wait_vm(int n) {
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // (stricter: wait for all)
   }
 }
+// lgkmcnt(0) with the other counters left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// BK: K step (elements); S: pipeline stages. Rows of a stage are BK * 2 bytes
-// in CH chunks of 16 bytes; chunk c of row R sits in slot c ^ (R / 2 mod CH).
-template <int BK, int S>
+// BK: K step (elements). Two stages; rows of a stage are BK * 2 bytes in CH
+// chunks of 16 bytes; chunk c of row R sits in slot c ^ (R / 2 mod CH).
+//
+// Matrix-core schedule: a wave's fragments are double-buffered over the K
+// sub-steps of 16 and across steps. In each sub-step the wave issues one
+// MFMA (its operand wait then covers only the reads issued during the
+// previous sub-step), then the next sub-step's fragment reads, then the other
+// seven MFMAs, so LDS latency hides behind matrix-core work. In the last
+// sub-step of step s, after four MFMAs, every wave has read all of step s:
+// it waits for its copies of step s + 1, meets the others at the barrier,
+// refills the stage of step s with step s + 2 and reads the first fragments
+// of step s + 1 while the remaining four MFMAs run.
+template <int BK>
 __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArgs a) {
   constexpr int kRowBytes = BK * 2;
   constexpr int CH = kRowBytes / 16;                 // chunks per row
@@ -308,9 +320,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   constexpr int kCopiesPerWave = 2 * kCopiesPerTile / 8;  // per step
   constexpr int kTileBytes = kBigM * kRowBytes;
   constexpr int kStageBytes = 2 * kTileBytes;
-  static_assert(kBigM == kBigN && BK % 16 == 0 && (CH & (CH - 1)) == 0, "tile shape");
+  constexpr int KK = BK / 16;                         // sub-steps per step
+  static_assert(kBigM == kBigN && BK % 16 == 0 && (CH & (CH - 1)) == 0 && KK >= 2, "tile shape");
   static_assert(kCopiesPerWave * 8 == 2 * kCopiesPerTile, "copies per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[S * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
@@ -332,8 +345,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   const int64_t p_row = static_cast<int64_t>(L.ldp) * 2, a_row = static_cast<int64_t>(L.d_in) * 2;
   // 16 consecutive rows (the rows a 16-lane group reads) cover both halves
   // of the 64 banks with 8 different slots each
-  auto slot_p = [](int R, int c) { return c ^ ((R >> 1) & (CH - 1)); };
-  auto slot_a = slot_p;
+  auto slot = [](int R, int c) { return c ^ ((R >> 1) & (CH - 1)); };
 
   // Copies K step `step` into stage `stage`: copy q of wave w fills row
   // block g = q * 8 + w (P blocks first, then A blocks); lane l writes slot
@@ -341,14 +353,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   auto issue = [&](int step, int stage) {
     char* sb = smem + stage * kStageBytes;
     const int64_t kb = static_cast<int64_t>(s_begin + step) * kRowBytes;
-    const int rl = lane / CH, slot = lane % CH;
+    const int rl = lane / CH, sl = lane % CH;
 #pragma unroll
     for (int q = 0; q < kCopiesPerWave; ++q) {
       const int g = q * 8 + wave;
       const bool is_a = g >= kCopiesPerTile;
       const int gi = is_a ? g - kCopiesPerTile : g;
       const int R = gi * kRowsPerCopy + rl;
-      const int c = is_a ? slot_a(R, slot) : slot_p(R, slot);  // the swizzle is an involution
+      const int c = slot(R, sl);  // the swizzle is an involution
       const char* src = (is_a ? Ab + R * a_row : Pb + R * p_row) + kb + c * 16;
       char* dst = sb + (is_a ? kTileBytes : 0) + gi * 1024;
       // (C casts: they are the address-space conversions)
@@ -359,36 +371,60 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   Acc<4, 2> acc;
   acc.zero();
   const int r32 = lane & 31, kh = lane >> 5;
-#pragma unroll
-  for (int q = 0; q < S - 1; ++q)
-    if (q < n_steps) issue(q, q);
-  for (int s = 0; s < n_steps; ++s) {
-    // step s has landed when at most the later issued steps are in flight
-    wait_vm(min(S - 2, n_steps - 1 - s) * kCopiesPerWave);
-    lds_barrier();  // every wave's copies of step s landed; step s - 1's reads are done
-    if (s + S - 1 < n_steps) issue(s + S - 1, (s + S - 1) % S);
-    const char* sP = smem + (s % S) * kStageBytes;
+  // fragments of sub-step kk of the step in stage `stage`: this lane's
+  // 16-byte chunk is k = 16 kk + 8 kh
+  auto read_frags = [&](int stage, int kk, bf16x8* af, bf16x8* bfr) {
+    const char* sP = smem + stage * kStageBytes;
     const char* sA = sP + kTileBytes;
+    const int c = 2 * kk + kh;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = 2 * kk + kh;  // this lane's 16-byte chunk: k = 16 kk + 8 kh
-      bf16x8 af[4], bfr[2];
+    for (int mb = 0; mb < 4; ++mb) {
+      const int j = 128 * wm + 32 * mb + r32;
+      af[mb] = *reinterpret_cast<const bf16x8*>(sP + j * kRowBytes + slot(j, c) * 16);
+    }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int j = 128 * wm + 32 * mb + r32;
-        af[mb] = *reinterpret_cast<const bf16x8*>(sP + j * kRowBytes + slot_p(j, c) * 16);
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = 64 * wn + 32 * nb + r32;
+      bfr[nb] = *reinterpret_cast<const bf16x8*>(sA + n * kRowBytes + slot(n, c) * 16);
+    }
+  };
+  // MFMAs q0 .. q1 - 1 of a sub-step's eight (q = 2 mb + nb)
+  auto mma = [&](const bf16x8* af, const bf16x8* bfr, int q0, int q1) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q >= q0 && q < q1)
+        acc.v[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            af[q >> 1], bfr[q & 1], acc.v[q >> 1][q & 1], 0, 0, 0);
+  };
+
+  bf16x8 fa[2][4], fb[2][2];
+  if (n_steps > 0) {
+    issue(0, 0);
+    wait_vm(0);
+    lds_barrier();
+    if (n_steps > 1) issue(1, 1);
+    read_frags(0, 0, fa[0], fb[0]);
+  }
+  for (int s = 0; s < n_steps; ++s) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      const int first = kk + 1 < KK ? 1 : 4;
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa[cur], fb[cur], 0, first);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < KK) {
+        read_frags(s & 1, kk + 1, fa[nxt], fb[nxt]);
+      } else if (s + 1 < n_steps) {
+        wait_lgkm0();  // this wave's reads of stage s & 1 are complete
+        wait_vm(0);    // its copies of step s + 1 landed
+        lds_barrier();
+        if (s + 2 < n_steps) issue(s + 2, s & 1);
+        read_frags((s + 1) & 1, 0, fa[nxt], fb[nxt]);
       }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int n = 64 * wn + 32 * nb + r32;
-        bfr[nb] = *reinterpret_cast<const bf16x8*>(sA + n * kRowBytes + slot_a(n, c) * 16);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb],
-                                                                 acc.v[mb][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa[cur], fb[cur], first, 8);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -1506,7 +1542,7 @@ static hipError_t launch_proj_ng(const ProjArgs& a, bool bf16_in, bool vec, hipS
 
 hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
   if (a.big) {
-    hipLaunchKernelGGL((proj_big_kernel<kBigK, kBigStages>), dim3(grid8(a.n_blocks)),
+    hipLaunchKernelGGL((proj_big_kernel<kBigK>), dim3(grid8(a.n_blocks)),
                        dim3(2 * kThreads), 0, s, a);
     return hipGetLastError();
   }
