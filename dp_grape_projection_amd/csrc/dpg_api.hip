@@ -226,8 +226,13 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   p.big = dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN &&
           static_cast<uint64_t>(B) * r * p.ldt * 2 < (1ull << 32) &&
           static_cast<uint64_t>(BT) * 4 * kBigM < (1ull << 32);
+  // (its copies go through buffer resources: each layer's A and P within
+  // 32-bit offsets)
   for (int l = 0; l < n_layers; ++l)
-    if (layers[l].d_in % kBigK != 0) p.big = false;
+    if (layers[l].d_in % kBigK != 0 ||
+        static_cast<uint64_t>(BT) * layers[l].d_in * 2 >= (1ull << 32) ||
+        static_cast<uint64_t>(r) * round_up(layers[l].d_in, 8) * 2 >= (1ull << 32))
+      p.big = false;
   int64_t big_sps = 0;
   if (p.big) {
     const int64_t tiles = (r / kBigM) * (BT / kBigN), cus = target / 2;
@@ -355,9 +360,13 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // the launches, with the rounds of resident blocks counted in K steps
   // (plus two per block for the pipeline's fill).
   p.has_samp_big = dtype == DPG_BF16 && r % kBigM == 0 && T % kSampBigK == 0;
-  for (int l = 0; l < n_layers; ++l)  // (stored products: 32-bit offsets over 256 rows)
+  // (stored products: 32-bit offsets over 256 rows; copies through buffer
+  // resources: each layer's dY and Xt within 32-bit offsets)
+  if (static_cast<uint64_t>(B) * r * round_up(T, 8) * 2 >= (1ull << 32)) p.has_samp_big = false;
+  for (int l = 0; l < n_layers; ++l)
     if (layers[l].d_out % kBigN != 0 ||
-        static_cast<uint64_t>(layers[l].d_out) * 4 * kBigM >= (1ull << 32))
+        static_cast<uint64_t>(layers[l].d_out) * 4 * kBigM >= (1ull << 32) ||
+        static_cast<uint64_t>(B) * T * layers[l].d_out * 2 >= (1ull << 32))
       p.has_samp_big = false;
   if (p.has_samp_big) {
     SampPlan& b = p.samp_big;

@@ -18,6 +18,8 @@
 // and the update call runs
 //   prep    Adam on [r][d_out] (m, v in place; U row-major) and P regenerated
 //   back    W -= lr P^T U
+#include <type_traits>
+
 #include "dpg_device.hpp"
 #include "dpg_internal.hpp"
 
@@ -299,6 +301,24 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// One direct global-to-LDS copy of 16 bytes per lane through a buffer
+// resource: lane offset `voff` (kept in a register across a loop) plus the
+// block-uniform `soff`; the 1 KiB a wave copies lands at `lds` (uniform).
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                            uint32_t soff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff,
+                                           __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
+// 16-byte LDS read of a matrix-core fragment through a restrict-qualified
+// pointer: the alias-scope information lets the compiler keep the read clear
+// of the direct global-to-LDS copies in flight (without it, it may wait for
+// all of them first; the kernels order copies and reads themselves).
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* __restrict__ p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ float lds_read_f32(const float* __restrict__ p) { return *p; }
+
 // BK: K step (elements). Two stages; rows of a stage are BK * 2 bytes in CH
 // chunks of 16 bytes; chunk c of row R sits in slot c ^ (R / 2 mod CH).
 //
@@ -340,8 +360,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   const int s_begin = split * L.steps_per_split;
   const int s_end = min(n_steps_all, s_begin + L.steps_per_split);
   const int n_steps = s_end - s_begin;
-  const char* Pb = static_cast<const char*>(L.P) + static_cast<int64_t>(j0) * L.ldp * 2;
-  const char* Ab = static_cast<const char*>(L.A) + static_cast<int64_t>(n0) * L.d_in * 2;
   const int64_t p_row = static_cast<int64_t>(L.ldp) * 2, a_row = static_cast<int64_t>(L.d_in) * 2;
   // 16 consecutive rows (the rows a 16-lane group reads) cover both halves
   // of the 64 banks with 8 different slots each
@@ -349,22 +367,31 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
 
   // Copies K step `step` into stage `stage`: copy q of wave w fills row
   // block g = q * 8 + w (P blocks first, then A blocks); lane l writes slot
-  // l % CH of row l / CH of the block.
+  // l % CH of row l / CH of the block, loading the chunk that the swizzle
+  // puts there (it is an involution). A block's index has the parity of w,
+  // so each lane's offset within its block is the same for every copy of a
+  // wave and stays in a register: copies go through buffer resources on P
+  // and A (the plan keeps both within 32-bit offsets), the block and step in
+  // the uniform offset.
+  static_assert(CH == 8 && kRowsPerCopy == 8 && kCopiesPerTile % 2 == 0, "copy layout");
+  const __amdgpu_buffer_rsrc_t rsP = tile_rsrc(L.P), rsA = tile_rsrc(L.A);
+  const uint32_t p_rb = static_cast<uint32_t>(p_row), a_rb = static_cast<uint32_t>(a_row);
+  const uint32_t chunk = static_cast<uint32_t>(((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) << 4);
+  const uint32_t voffP = static_cast<uint32_t>(lane >> 3) * p_rb + chunk;
+  const uint32_t voffA = static_cast<uint32_t>(lane >> 3) * a_rb + chunk;
   auto issue = [&](int step, int stage) {
     char* sb = smem + stage * kStageBytes;
-    const int64_t kb = static_cast<int64_t>(s_begin + step) * kRowBytes;
-    const int rl = lane / CH, sl = lane % CH;
+    const uint32_t kb = static_cast<uint32_t>(s_begin + step) * kRowBytes;
 #pragma unroll
     for (int q = 0; q < kCopiesPerWave; ++q) {
       const int g = q * 8 + wave;
       const bool is_a = g >= kCopiesPerTile;
       const int gi = is_a ? g - kCopiesPerTile : g;
-      const int R = gi * kRowsPerCopy + rl;
-      const int c = slot(R, sl);  // the swizzle is an involution
-      const char* src = (is_a ? Ab + R * a_row : Pb + R * p_row) + kb + c * 16;
-      char* dst = sb + (is_a ? kTileBytes : 0) + gi * 1024;
-      // (C casts: they are the address-space conversions)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+      const uint32_t row0 = static_cast<uint32_t>((is_a ? n0 : j0) + gi * kRowsPerCopy);
+      if (is_a)
+        copy_to_lds(rsA, voffA, row0 * a_rb + kb, sb + kTileBytes + gi * 1024);
+      else
+        copy_to_lds(rsP, voffP, row0 * p_rb + kb, sb + gi * 1024);
     }
   };
 
@@ -380,12 +407,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int j = 128 * wm + 32 * mb + r32;
-      af[mb] = *reinterpret_cast<const bf16x8*>(sP + j * kRowBytes + slot(j, c) * 16);
+      af[mb] = lds_read_b128(sP + j * kRowBytes + slot(j, c) * 16);
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int n = 64 * wn + 32 * nb + r32;
-      bfr[nb] = *reinterpret_cast<const bf16x8*>(sA + n * kRowBytes + slot(n, c) * 16);
+      bfr[nb] = lds_read_b128(sA + n * kRowBytes + slot(n, c) * 16);
     }
   };
   // MFMAs q0 .. q1 - 1 of a sub-step's eight (q = 2 mb + nb)
@@ -782,8 +809,11 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   static_assert(kTileBytes == BK * kRowB && kBigM == kBigN, "equal square tiles");
   static_assert(kCopies * 8 == 2 * kBlocksA && kCopies % 2 == 0, "copies per wave");
   static_assert(CHA == 8 && CHB == 32, "swizzles assume 128- and 512-byte rows");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
-  __shared__ float s_grp[SUM ? kSumMaxGroup : 1];
+  // the stages, then (sum mode) the group's clip factors: one LDS object
+  // (with the factors in an array of their own the compiler made the main
+  // loop's fragment reads wait for the copies in flight)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes + (SUM ? kSumMaxGroup * 4 : 0)];
+  float* s_grp = reinterpret_cast<float*>(smem + 2 * kStageBytes);
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const int li = find_layer(a.L, a.n_layers, lb);
@@ -800,32 +830,36 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   const int i_end = min(a.B, i_begin + a.per_block);
   const int kc = a.T / BK;  // steps per sample
   const int n_steps = (i_end - i_begin) * kc;
-  const char* Xt = static_cast<const char*>(L.Xt);
-  const char* dY = static_cast<const char*>(L.dY);
-  const int64_t x_row = static_cast<int64_t>(a.ldt) * 2, y_row = static_cast<int64_t>(L.d_out) * 2;
   // 16 consecutive rows cover both halves of the 64 banks with 8 slots each
   auto slot_a = [](int R, int c) { return c ^ ((R >> 1) & (CHA - 1)); };
 
   // Copies step `step` into stage `stage`: copy q of wave w fills 1 KiB
   // block q * 8 + w (Xt blocks of 8 rows first, then dY blocks of 2 rows);
-  // lane l writes the block's 16-byte slot l.
+  // lane l writes the block's 16-byte slot l, loading the chunk that the
+  // swizzle puts there (the swizzles are involutions). A block's index has
+  // the parity of w, so each lane's offset within its block is fixed for a
+  // wave and stays in a register; copies go through buffer resources on the
+  // layer's Xt and dY (the plan keeps both within 32-bit offsets), the
+  // sample, step and block in the uniform offset.
+  const __amdgpu_buffer_rsrc_t rsX = tile_rsrc(L.Xt), rsY = tile_rsrc(L.dY);
+  const uint32_t xr = static_cast<uint32_t>(a.ldt) * 2u, yr = static_cast<uint32_t>(L.d_out) * 2u;
+  const uint32_t voffX = static_cast<uint32_t>(lane >> 3) * xr +
+                         static_cast<uint32_t>(((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) << 4);
+  const uint32_t voffY = static_cast<uint32_t>(lane >> 5) * yr +
+                         static_cast<uint32_t>(((lane & 31) ^ (4 * ((2 * (wave & 1) + (lane >> 5)) & 3))) << 4);
   auto issue = [&](int step, int stage) {
     char* sb = smem + stage * kStageBytes;
     const int i = i_begin + step / kc, k0 = (step % kc) * BK;
-    const char* Xb = Xt + (static_cast<int64_t>(i) * a.r + j0) * x_row + k0 * 2;
-    const char* Yb = dY + (static_cast<int64_t>(i) * a.T + k0) * y_row + n0 * 2;
+    const uint32_t bx = static_cast<uint32_t>(i * a.r + j0) * xr + static_cast<uint32_t>(k0) * 2u;
+    const uint32_t by = static_cast<uint32_t>(i * a.T + k0) * yr + static_cast<uint32_t>(n0) * 2u;
 #pragma unroll
     for (int q = 0; q < kCopies; ++q) {
       const int blk = q * 8 + wave;
-      const char* src;
-      if (q < kCopies / 2) {
-        const int R = blk * (1024 / kRowA) + lane / CHA;
-        src = Xb + R * x_row + slot_a(R, lane % CHA) * 16;  // the swizzles are involutions
-      } else {
-        const int R = (blk - kBlocksA) * (1024 / kRowB) + lane / CHB;
-        src = Yb + R * y_row + kmajor_slot(R, lane % CHB) * 16;
-      }
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(sb + blk * 1024), 16, 0, 0);
+      if (q < kCopies / 2)
+        copy_to_lds(rsX, voffX, bx + static_cast<uint32_t>(blk * (1024 / kRowA)) * xr, sb + blk * 1024);
+      else
+        copy_to_lds(rsY, voffY, by + static_cast<uint32_t>((blk - kBlocksA) * (1024 / kRowB)) * yr,
+                    sb + blk * 1024);
     }
   };
 
@@ -861,46 +895,77 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   float c = 0.0f;  // sum mode: factor the accumulator is expressed in
   bool on = true;  // sum mode: the current sample is accumulated
   const int r32 = lane & 31, kh = lane >> 5;
-  if (n_steps > 0) issue(0, 0);
-  for (int s = 0; s < n_steps; ++s) {
-    wait_vm(0);
-    lds_barrier();  // step s landed for every wave; step s - 1's reads are done
-    const char* sX = smem + (s & 1) * kStageBytes;
+  // fragments of sub-step kk of the step in stage `stage`: Xt rows (this
+  // lane's chunk t = 16 kk + 8 kh ..) and, through the transposing read,
+  // dY columns
+  auto read_frags = [&](int stage, int kk, bf16x8* af, bf16x8* bfr) {
+    const char* sX = smem + stage * kStageBytes;
     const char* sY = sX + kTileBytes;
-    // the B fragments of the whole step, read before the next step's copies
-    // are issued
-    bf16x8 bfr[BK / 16][2];
+    const int cx = 2 * kk + kh;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
+    for (int mb = 0; mb < 4; ++mb) {
+      const int j = 128 * wm + 32 * mb + r32;
+      af[mb] = lds_read_b128(sX + j * kRowA + slot_a(j, cx) * 16);
+    }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bfr[kk][nb] = frag_kmajor(sY, 16 * kk, 64 * wn + 32 * nb, lane);
-    if (s + 1 < n_steps) issue(s + 1, (s + 1) & 1);
+    for (int nb = 0; nb < 2; ++nb) bfr[nb] = frag_kmajor(sY, 16 * kk, 64 * wn + 32 * nb, lane);
+  };
+  auto mma = [&](const bf16x8* af, const bf16x8* bfr, int q0, int q1) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q >= q0 && q < q1)
+        acc.v[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            af[q >> 1], bfr[q & 1], acc.v[q >> 1][q & 1], 0, 0, 0);
+  };
+  // the schedule of proj_big_kernel: fragments double-buffered over the
+  // sub-steps and across steps, the stage wait and barrier in the middle of
+  // the last sub-step, the refill into the stage just read
+  constexpr int KK = BK / 16;
+  bf16x8 fa[2][4], fb[2][2];
+  if (n_steps > 0) {
+    issue(0, 0);
+    wait_vm(0);
+    lds_barrier();
+    if (n_steps > 1) issue(1, 1);
+    read_frags(0, 0, fa[0], fb[0]);
+  }
+  for (int s = 0; s < n_steps; ++s) {
     if (SUM && s % kc == 0) {
-      const float si = s_grp[s / kc];
+      const float si = lds_read_f32(s_grp + s / kc);
       on = si > 0.0f;
       if (on) {
         if (c != 0.0f && c != si) acc.scale(c / si);
         c = si;
       }
     }
-    if (on) {
+    // the step's body with and without its matrix-core work (a sample whose
+    // clip factor is 0 is read and waited for but not accumulated); two
+    // instances, so that the hot one has no branches between its MFMAs
+    auto body = [&](auto with_mma) {
+      constexpr bool M = decltype(with_mma)::value;
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int cx = 2 * kk + kh;  // this lane's Xt chunk: t = 16 kk + 8 kh ..
-        bf16x8 af[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const int j = 128 * wm + 32 * mb + r32;
-          af[mb] = *reinterpret_cast<const bf16x8*>(sX + j * kRowA + slot_a(j, cx) * 16);
+      for (int kk = 0; kk < KK; ++kk) {
+        const int cur = kk & 1, nxt = cur ^ 1;
+        const int first = kk + 1 < KK ? 1 : 4;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (M) mma(fa[cur], fb[cur], 0, first);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < KK) {
+          read_frags(s & 1, kk + 1, fa[nxt], fb[nxt]);
+        } else if (s + 1 < n_steps) {
+          wait_lgkm0();  // this wave's reads of stage s & 1 are complete
+          wait_vm(0);    // its copies of step s + 1 landed
+          lds_barrier();
+          if (s + 2 < n_steps) issue(s + 2, s & 1);
+          read_frags((s + 1) & 1, 0, fa[nxt], fb[nxt]);
         }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[kk][nb],
-                                                                   acc.v[mb][nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (M) mma(fa[cur], fb[cur], first, 8);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    if (on) body(std::true_type{});
+    else body(std::false_type{});
     if (!SUM && s % kc == kc - 1) {
       const int i = i_begin + s / kc;
       const float t = wave_sum(acc.sum_sq());
@@ -937,18 +1002,30 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   }
 
   if (SUM) {
-    // lane: column n0 + 64 wn + 32 nb + r32; registers i: rows
-    // 8 (i / 4) + 4 kh + i % 4 of its 32-row block
+    // the group's partial [r][d_out], through a buffer resource on the
+    // wave's 128 rows (lane: column n0 + 64 wn + 32 nb + r32; register q:
+    // row 32 mb + 8 (q / 4) + 4 kh + q % 4). One lane offset and uniform
+    // row offsets: per-element 64-bit addresses here raised the register
+    // pressure of the whole kernel enough that the main loop's fragment
+    // reads waited for the step's copies.
     acc.scale(c);
-    float* part = L.part + static_cast<int64_t>(g) * a.r * L.d_out;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(
+        L.part + (static_cast<int64_t>(g) * a.r + j0 + 128 * wm) * L.d_out);
+    const uint32_t row4 = static_cast<uint32_t>(L.d_out) * 4u;
+    const uint32_t lo = static_cast<uint32_t>(4 * kh) * row4 +
+                        static_cast<uint32_t>(n0 + 64 * wn + r32) * 4u;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = j0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * kh + (i & 3);
-          part[static_cast<int64_t>(j) * L.d_out + n0 + 64 * wn + 32 * nb + r32] = acc.v[mb][nb][i];
+        for (int q = 0; q < 16; ++q) {
+          const float x = acc.v[mb][nb][q];
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, x), rs, lo + 128u * nb,
+              __builtin_amdgcn_readfirstlane(
+                  static_cast<uint32_t>(32 * mb + 8 * (q >> 2) + (q & 3)) * row4),
+              0);
         }
   }
 }
