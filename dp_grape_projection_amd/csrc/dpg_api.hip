@@ -532,27 +532,34 @@ int enqueue_back(const dpg_layer_param* params, int l0, int l1, int32_t r,
       }
     }
   }
-  // Large bf16 back-projections (r over one step, a multiple of kSampBigK;
-  // d_in and d_out whole 256 x 256 tiles; 16-byte aligned rows): one 8-wave
-  // block per CU sweeps a run of column tiles, the run minimising (rounds of
-  // resident blocks) x (tiles per block) x (K steps per tile plus about four
-  // steps' worth of W traffic), ties to the longer run.
-  b.big = bf16 && r % kSampBigK == 0 && r > step_of(dtype);
+  // Large bf16 back-projections (r over one step, a multiple of kBackBigK;
+  // d_in whole 256-row tiles, d_out whole 128-column tiles; 16-byte aligned
+  // rows): 4-wave blocks, two per CU, each sweeping a run of column tiles;
+  // the run minimises (rounds of resident blocks) x (tiles per block) x (K
+  // steps per tile plus about eight steps' worth of W traffic), ties to the
+  // longer run, and is at most an eighth of every layer's column tiles, so
+  // that each group of 8 row tiles has at least 8 runs: the blocks one XCD
+  // runs at once then share 8 slices of P and 8 of U (the kernel's block
+  // order), instead of each re-reading a P slice of its own from HBM.
+  b.big = bf16 && r % kBackBigK == 0 && r > step_of(dtype);
   for (int l = l0; l < l1; ++l)
-    if (params[l].d_in % kBigM != 0 || params[l].d_out % kBigN != 0 ||
+    if (params[l].d_in % kBigM != 0 || params[l].d_out % kBackBigN != 0 ||
         !aligned(params[l].W, 16) || !aligned(P_of(l), 16) || !aligned(U_of(l), 16) ||
         (ldp_of(l) * elem_size(dtype)) % 16 != 0 ||
-        static_cast<uint64_t>(params[l].d_out) * 4 * kBigM >= (1ull << 32))  // W: 32-bit offsets
+        static_cast<uint64_t>(params[l].d_out) * 4 * kBigM >= (1ull << 32) ||  // W: 32-bit offsets
+        static_cast<uint64_t>(r) * ldp_of(l) * 2 >= (1ull << 32) ||          // P, U: buffer copies
+        static_cast<uint64_t>(r) * params[l].d_out * 2 >= (1ull << 32))
       b.big = 0;
   if (b.big) {
-    int64_t best = -1, max_nt = 1;
-    for (int l = l0; l < l1; ++l) max_nt = std::max<int64_t>(max_nt, params[l].d_out / kBigN);
-    const int64_t cus = target_blocks(dtype) / 2, kr = r / kSampBigK;
-    for (int64_t per = 1; per <= max_nt; ++per) {
+    int64_t best = -1, max_per = INT64_MAX;
+    for (int l = l0; l < l1; ++l)
+      max_per = std::min<int64_t>(max_per, std::max<int64_t>(1, params[l].d_out / kBackBigN / 8));
+    const int64_t resident = target_blocks(dtype), kr = r / kBackBigK;
+    for (int64_t per = 1; per <= max_per; ++per) {
       int64_t nb = 0;
       for (int l = l0; l < l1; ++l)
-        nb += (params[l].d_in / kBigM) * ceil_div(params[l].d_out / kBigN, per);
-      const int64_t cost = ceil_div(nb, cus) * per * (kr + 4);
+        nb += (params[l].d_in / kBigM) * ceil_div(params[l].d_out / kBackBigN, per);
+      const int64_t cost = ceil_div(nb, resident) * per * (kr + 8);
       if (best < 0 || cost <= best) {
         best = cost;
         b.res_tiles = static_cast<int32_t>(per);
@@ -568,7 +575,7 @@ int enqueue_back(const dpg_layer_param* params, int l0, int l1, int32_t r,
       L.d_in = static_cast<int32_t>(params[l].d_in);
       L.d_out = static_cast<int32_t>(params[l].d_out);
       L.m_tiles = static_cast<int32_t>(params[l].d_in / kBigM);
-      L.n_tiles = static_cast<int32_t>(params[l].d_out / kBigN);
+      L.n_tiles = static_cast<int32_t>(params[l].d_out / kBackBigN);
       L.n_chunks = static_cast<int32_t>(ceil_div(L.n_tiles, b.res_tiles));
       L.block0 = blocks;
       blocks += L.m_tiles * L.n_chunks;

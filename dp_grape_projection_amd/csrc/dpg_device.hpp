@@ -41,6 +41,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
                                            static_cast<int>(0xFFFFFFFFu), 0x00020000);
 }
 
+// Cache-policy operand of the buffer load and store builtins for data read
+// or written once (the nt bit on gfx950): such lines are the first the L2
+// evicts, so a stream of them does not push out operands that are re-read.
+constexpr int kNonTemporal = 2;
+
 // ---------------------------------------------------------------- random --
 
 // Ten Philox rounds: each round multiplies c0 and c2 by the two round

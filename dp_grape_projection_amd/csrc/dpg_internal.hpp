@@ -24,6 +24,9 @@ constexpr int kSumBatch = 8;
 // loads in two stages, 8 waves per block.
 constexpr int kBigM = 256, kBigN = 256, kBigK = 64;
 constexpr int kSampBigK = 64;  // K step (over t) of the large norm and sum kernel
+// Large back-projection: 256 (d_in) x 128 (d_out) tiles, K steps of 32 over r,
+// 4-wave blocks, two per CU.
+constexpr int kBackBigN = 128, kBackBigK = 32;
 // The sum pass folds the per-sample norm and clip factor into its prologue
 // when a group holds at most this many samples and each sample at most this
 // many norm partials.
@@ -225,7 +228,7 @@ struct BackArgs {
   int32_t res_tiles;  // r within one step: a block keeps its P tile in LDS
                       // and sweeps this many column tiles (0: one tile); with
                       // big, the run of column tiles of a block
-  int32_t big;        // back_big_kernel: kBigM x kBigN tiles, steps of kSampBigK
+  int32_t big;        // back_big_kernel: kBigM x kBackBigN tiles, steps of kBackBigK
 };
 
 // Records `msg` as the calling thread's last error (dpg_last_error) and

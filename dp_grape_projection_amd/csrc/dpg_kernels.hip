@@ -780,19 +780,23 @@ __device__ __forceinline__ v4i16 lds_read_tr(const char* __restrict__ p) {
 }
 
 // Matrix-core operand of a 32x32x16 product from a k-major LDS tile (rows of
-// 512 bytes, kmajor_slot swizzle): lane l receives rows k0 + 8 (l / 32) ..
-// + 7 of column c0 + l % 32. In each group of 16 lanes, lane q addresses four
-// consecutive columns of row k0 + 8 (l / 32) + 4 h + q / 4; the transposing
-// read hands lane j element j % 4 of the values lanes j / 4, 4 + j / 4, ...
-// addressed, which is four consecutive rows of one column.
+// ROW bytes, 256 or 512, kmajor_slot swizzle): lane l receives rows k0 + 8
+// (l / 32) .. + 7 of column c0 + l % 32. In each group of 16 lanes, lane q
+// addresses four consecutive columns of row k0 + 8 (l / 32) + 4 h + q / 4;
+// the transposing read hands lane j element j % 4 of the values lanes j / 4,
+// 4 + j / 4, ... addressed, which is four consecutive rows of one column.
+// The 32 lanes of a half-wave read four rows of 64 bytes; the swizzle puts
+// them in 16 different 16-byte bank groups for either row length.
+template <int ROW = 512>
 __device__ __forceinline__ bf16x8 frag_kmajor(const char* tile, int k0, int c0, int lane) {
+  static_assert(ROW == 256 || ROW == 512, "rows of 16 or 32 chunks");
   const int q16 = lane & 15, nh = (lane >> 4) & 1, kh = lane >> 5;
   const int n = c0 + 16 * nh + 4 * (q16 & 3);
   v4i16 h[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = k0 + 8 * kh + 4 * i + (q16 >> 2);
-    h[i] = lds_read_tr(tile + t * 512 + kmajor_slot(t, n >> 3) * 16 + (n & 7) * 2);
+    h[i] = lds_read_tr(tile + t * ROW + kmajor_slot(t, n >> 3) * 16 + (n & 7) * 2);
   }
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
@@ -1408,30 +1412,40 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
   }
 }
 
-// W -= lr P^T U in 256 x 256 tiles (rows m of W over d_in, columns n over
-// d_out) for bf16 with d_in, d_out whole tiles and r a multiple of kSampBigK:
-// one 8-wave block per CU sweeps a run of column tiles of one row tile, its K
-// steps over r running on from tile to tile, with two stages of direct
-// global-to-LDS copies. P [r][d_in] and U [r][d_out] are k-major and stay so
-// in LDS (512-byte rows); both matrix-core operands come from the
-// transposing LDS read. A tile's W update runs while the copies of the next
-// tile's first step are in flight; half of its W is fetched before the
-// tile's last step. Waves are 2 (m) x 4 (n), each 128 x 64.
-__global__ __launch_bounds__(2 * kThreads, 1) void back_big_kernel(const BackArgs a) {
-  constexpr int BK = kSampBigK;
-  constexpr int kRow = kBigN * 2;                       // 512-byte rows
-  constexpr int kTileBytes = BK * kRow;
-  constexpr int kBlocks = kTileBytes / 1024;            // 1 KiB copies per tile
-  constexpr int kCopies = 2 * kBlocks / 8;              // per wave and step
-  constexpr int kStageBytes = 2 * kTileBytes;
-  static_assert(kBigM == kBigN && kRow == 512, "k-major tiles of 512-byte rows");
-  static_assert(kCopies * 8 == 2 * kBlocks && kCopies % 2 == 0, "copies per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+// W -= lr P^T U in 256 x 128 tiles (rows m of W over d_in, columns n over
+// d_out) for bf16 with d_in a multiple of 256, d_out of 128 and r of 32.
+// Blocks of 4 waves (2 (m) x 2 (n), each 128 x 64), two per CU, so that one
+// block's read-modify-write of W (the HBM traffic that bounds this pass)
+// runs while the other block's matrix cores work. A block sweeps a run of
+// column tiles of one row tile, its K steps of 32 over r running on from
+// tile to tile, with two stages of direct global-to-LDS copies (a stage is
+// refilled as soon as every wave has read it). P [r][d_in] and U [r][d_out]
+// are k-major and stay so in LDS (rows of 512 and 256 bytes); both
+// matrix-core operands come from the transposing read. W goes through a
+// buffer resource, one 32-row block at a time, the next block's loads in
+// flight while the current one is stored.
+__global__ __launch_bounds__(kThreads, 2) void back_big_kernel(const BackArgs a) {
+  constexpr int BK = kBackBigK;
+  constexpr int kRowP = kBigM * 2, kRowU = kBackBigN * 2;      // 512- and 256-byte rows
+  constexpr int kTileP = BK * kRowP, kTileU = BK * kRowU;     // 16 and 8 KiB
+  constexpr int kStage = kTileP + kTileU;
+  constexpr int kCopiesP = kTileP / 1024 / 4, kCopiesU = kTileU / 1024 / 4;  // per wave and step
+  static_assert(kCopiesP == 4 && kCopiesU == 2 && BK == 32, "copy layout");
+  constexpr int NS = 3;  // stages: copies run up to two steps ahead
+  __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const BackLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  // Blocks of a layer: groups of (up to) 8 row tiles; in a group, each run
+  // of column tiles for each of its rows, the rows varying fastest. The
+  // blocks an XCD runs at once are consecutive, so they cover about 8 rows
+  // by 8 runs: 8 slices of P, each read again for every tile of its runs,
+  // and 8 slices of U, each read by 8 blocks at about the same time, stay
+  // in that XCD's L2.
   const int local = lb - L.block0;
-  const int mt = local % L.m_tiles, ch = local / L.m_tiles;
+  const int grp = local / (8 * L.n_chunks), rem = local - grp * 8 * L.n_chunks;
+  const int g = min(8, L.m_tiles - 8 * grp);
+  const int ch = rem / g, mt = 8 * grp + (rem - ch * g);
   const int nt0 = ch * a.res_tiles, nt1 = min(L.n_tiles, nt0 + a.res_tiles);
   const int m0 = mt * kBigM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1439,36 +1453,41 @@ __global__ __launch_bounds__(2 * kThreads, 1) void back_big_kernel(const BackArg
   const int r32 = lane & 31, kh = lane >> 5;
   const int kr = a.r / BK;  // steps per tile
   const int n_steps = (nt1 - nt0) * kr;
-  const char* P = static_cast<const char*>(L.P) + static_cast<int64_t>(m0) * 2;
-  const char* U = static_cast<const char*>(L.U);
-  const int64_t p_row = static_cast<int64_t>(L.ldp) * 2, u_row = static_cast<int64_t>(L.d_out) * 2;
+  const uint32_t p_rb = static_cast<uint32_t>(L.ldp) * 2u, u_rb = static_cast<uint32_t>(L.d_out) * 2u;
 
-  // Copies step `step` into stage `stage`: copy q of wave w fills 1 KiB
-  // block q * 8 + w (P blocks first, then U blocks), rows 2 b and 2 b + 1 of
-  // its operand (b the block's index within the operand); lane l writes slot
-  // l % 32 of row 2 b + l / 32. Block indices of a wave share their parity,
-  // so each lane's byte offset within its row pair is fixed.
-  const int lr = lane >> 5, lc = lane & 31;
-  const int sw = kmajor_slot(2 * (wave & 1) + lr, lc) * 16;  // the swizzle is an involution
-  const int off_p = lr * static_cast<int>(p_row) + sw, off_u = lr * static_cast<int>(u_row) + sw;
+  // Copies step `step` into stage `stage`: copy q < 4 of wave w fills P
+  // block q * 4 + w (k rows 2 b and 2 b + 1, 512 bytes each), copy q >= 4 U
+  // block (q - 4) * 4 + w (k rows 4 b .. 4 b + 3, 256 bytes each); lane l
+  // writes 16-byte slot l of the block, loading the chunk the swizzle puts
+  // there (an involution). The lane offsets are fixed for a wave (a P block
+  // has the parity of w; the U swizzle does not depend on the block), so
+  // they stay in registers; buffer resources on P and U (the plan keeps
+  // both within 32-bit offsets).
+  const __amdgpu_buffer_rsrc_t rsP = tile_rsrc(L.P), rsU = tile_rsrc(L.U);
+  const uint32_t voffP = static_cast<uint32_t>(lane >> 5) * p_rb +
+                         static_cast<uint32_t>(((lane & 31) ^ (4 * ((2 * (wave & 1) + (lane >> 5)) & 3))) << 4);
+  const uint32_t voffU = static_cast<uint32_t>(lane >> 4) * u_rb +
+                         static_cast<uint32_t>(((lane & 15) ^ (4 * ((lane >> 4) & 3))) << 4);
   auto issue = [&](int step, int stage) {
-    char* sb = smem + stage * kStageBytes;
-    const int nt = nt0 + step / kr, k0 = (step % kr) * BK;
-    const char* Pb = P + k0 * p_row;
-    const char* Ub = U + k0 * u_row + static_cast<int64_t>(nt) * kRow;
+    char* sb = smem + stage * kStage;
+    const int nt = nt0 + step / kr;
+    const uint32_t k0 = static_cast<uint32_t>((step % kr) * BK);
 #pragma unroll
-    for (int q = 0; q < kCopies; ++q) {
-      const int blk = q * 8 + wave;
-      const char* src = q < kCopies / 2 ? Pb + 2 * blk * p_row + off_p
-                                        : Ub + 2 * (blk - kBlocks) * u_row + off_u;
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(sb + blk * 1024), 16, 0, 0);
+    for (int q = 0; q < kCopiesP; ++q) {
+      const int blk = q * 4 + wave;
+      copy_to_lds(rsP, voffP, (k0 + 2u * blk) * p_rb + static_cast<uint32_t>(m0) * 2u, sb + blk * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < kCopiesU; ++q) {
+      const int blk = q * 4 + wave;
+      copy_to_lds(rsU, voffU, (k0 + 4u * blk) * u_rb + static_cast<uint32_t>(nt * kBackBigN) * 2u,
+                  sb + kTileP + blk * 1024);
     }
   };
 
-  // lane: columns n + 32 nb; registers i: rows 8 (i / 4) + 4 kh + i % 4 of
-  // each 32-row block mb. W is updated one row block at a time, the next
-  // block's load in flight while the current one is stored, through a buffer
-  // resource on the wave's 128 rows: one per-lane offset, the rest uniform.
+  // lane: columns 64 wn + 32 nb + r32 of the tile; registers i: rows
+  // 8 (i / 4) + 4 kh + i % 4 of each 32-row block mb, of the wave's 128
+  // rows: one lane offset, the rest uniform
   const __amdgpu_buffer_rsrc_t w_rs =
       tile_rsrc(L.W + static_cast<int64_t>(m0 + 128 * wm) * L.d_out);
   const uint32_t row4 = static_cast<uint32_t>(L.d_out) * 4u;
@@ -1477,7 +1496,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void back_big_kernel(const BackArg
   auto w_soff = [&](int nt, int mb, int i) {
     return __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(32 * mb + 8 * (i >> 2) + (i & 3)) * row4 +
-        static_cast<uint32_t>(nt) * (kBigN * 4u));
+        static_cast<uint32_t>(nt) * (kBackBigN * 4u));
   };
   typedef float WBlock[2][16];
   auto load_w = [&](int nt, int mb, WBlock& w) {
@@ -1486,38 +1505,51 @@ __global__ __launch_bounds__(2 * kThreads, 1) void back_big_kernel(const BackArg
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         w[nb][i] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(w_rs, w_lane + 128u * nb, w_soff(nt, mb, i), 0));
+            float, __builtin_amdgcn_raw_buffer_load_b32(w_rs, w_lane + 128u * nb, w_soff(nt, mb, i), kNonTemporal));
   };
   Acc<4, 2> acc;
   auto store_w = [&](int nt, int mb, const WBlock& w) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __builtin_bit_cast(uint32_t, fmaf(-a.lr, acc.v[mb][nb][i], w[nb][i])), w_rs,
-            w_lane + 128u * nb, w_soff(nt, mb, i), 0);
+      for (int i = 0; i < 16; ++i) {
+        const float x = fmaf(-a.lr, acc.v[mb][nb][i], w[nb][i]);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), w_rs,
+                                              w_lane + 128u * nb, w_soff(nt, mb, i), kNonTemporal);
+      }
   };
 
+  // vmcnt(n) for the copy counts below (6 copies a wave and step)
+  auto wait_copies = [](int n) {
+    if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
+    else if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F76);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+  constexpr int kCopies = kCopiesP + kCopiesU;
   acc.zero();
-  if (n_steps > 0) issue(0, 0);
+  if (n_steps > 0) {
+    // steps 0 .. NS - 1 in flight; wait for step 0
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+      if (q < n_steps) issue(q, q);
+    wait_copies((min(NS, n_steps) - 1) * kCopies);
+    lds_barrier();
+  }
   WBlock w0, w1;
+  int stage = 0;
   for (int s = 0; s < n_steps; ++s) {
-    wait_vm(0);
-    lds_barrier();  // step s landed for every wave; step s - 1's reads are done
-    if (s + 1 < n_steps) issue(s + 1, (s + 1) & 1);
     const bool last = s % kr == kr - 1;
     const int nt = nt0 + s / kr;
     if (last) load_w(nt, 0, w0);
-    const char* sP = smem + (s & 1) * kStageBytes;
-    const char* sU = sP + kTileBytes;
+    const char* sP = smem + stage * kStage;
+    const char* sU = sP + kTileP;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) af[mb] = frag_kmajor(sP, 16 * kk, 128 * wm + 32 * mb, lane);
+      for (int mb = 0; mb < 4; ++mb) af[mb] = frag_kmajor<kRowP>(sP, 16 * kk, 128 * wm + 32 * mb, lane);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bfr[nb] = frag_kmajor(sU, 16 * kk, 64 * wn + 32 * nb, lane);
+      for (int nb = 0; nb < 2; ++nb) bfr[nb] = frag_kmajor<kRowU>(sU, 16 * kk, 64 * wn + 32 * nb, lane);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -1525,6 +1557,19 @@ __global__ __launch_bounds__(2 * kThreads, 1) void back_big_kernel(const BackArg
           acc.v[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb],
                                                                  acc.v[mb][nb], 0, 0, 0);
     }
+    if (s + 1 < n_steps) {
+      wait_lgkm0();  // this wave's reads of stage `stage` are complete
+      // its copies of step s + 1 landed: loads return in order, so the
+      // copies issued after them (steps s + 2 .. s + NS - 1) may stay in
+      // flight, unless W stores are outstanding too (the previous step ended
+      // a tile): stores may complete out of order, so then wait for all
+      if (s % kr == 0 && s > 0) wait_vm(0);
+      else wait_copies((min(s + NS - 1, n_steps - 1) - (s + 1)) * kCopies);
+      lds_barrier();
+      // every wave has read stage `stage`: it takes step s + NS
+      if (s + NS < n_steps) issue(s + NS, stage);
+    }
+    stage = stage + 1 == NS ? 0 : stage + 1;
     if (last) {
       load_w(nt, 1, w1);
       store_w(nt, 0, w0);
@@ -1721,7 +1766,7 @@ hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
 hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s) {
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (a.big) {
-    hipLaunchKernelGGL(back_big_kernel, g, dim3(2 * kThreads), 0, s, a);
+    hipLaunchKernelGGL(back_big_kernel, g, dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   if (a.res_tiles > 0) {
