@@ -14,8 +14,8 @@ Sources (gist.science pages; cited by page title and section):
            and the closing paragraph of Methodology (training loop).
   [RC]     "DP-SGD Eficiente para LLMs con Recorte Aleatorizado" (arXiv
            2605.24879 explainer), Methodology - core mechanism (trace
-           identity, Hutchinson estimator) and Algorithmic flow step 4
-           (clip factor min(C/n, 1)).
+           identity, Hutchinson estimator) and Algorithmic flow steps 3-4
+           (norm estimation; clip factor min(C/n, 1)); oracle.randclip.
 
 Parity status of each function is stated in its docstring. Readings where the
 pages are silent are listed in the module docstring of oracle.dpgrape.
@@ -27,4 +27,7 @@ from .dpgrape import (  # noqa: F401
     project_clip_noise, adam_update, backproject_delta, adam_backproject,
     naive_privatise_then_project, sample_norms, clip_scale,
     projection_rows, noise_rows, g_priv_rows,
+)
+from .randclip import (  # noqa: F401
+    TAG_PROBE, probe_matrix, hutchinson_layer, estimated_norms, rc_clip_factors,
 )
