@@ -34,7 +34,7 @@ EXPORTED = (
     "dpg_project_layer_workspace_size", "dpg_project_layer",
     "dpg_clip_workspace_size", "dpg_clip_sum_noise",
     "dpg_step_workspace_size", "dpg_private_step", "dpg_private_step_static",
-    "dpg_static_scratch_bytes",
+    "dpg_static_scratch_bytes", "dpg_rc_norms_workspace_size", "dpg_rc_norms",
     "dpg_status_string", "dpg_last_error", "dpg_version",
     "dpg_timing_enable", "dpg_timing_read", "dpg_kernel_name",
 )
@@ -93,6 +93,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dpg_project_clip_noise.argtypes = [
         ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, f64, f64, u64,
         u64, u64, vp, vp, sz, vp]
+    lib.dpg_rc_norms_workspace_size.argtypes = [
+        ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, ctypes.POINTER(sz)]
+    lib.dpg_rc_norms.argtypes = [
+        ctypes.POINTER(LayerGrad), i32, i64, i64, i32, i32, f64, u64, u64, vp, vp,
+        vp, sz, vp]
     lib.dpg_adam_workspace_size.argtypes = [
         ctypes.POINTER(LayerParam), i32, i32, i32, ctypes.POINTER(sz)]
     lib.dpg_adam_backproject.argtypes = [
@@ -335,6 +340,48 @@ def dpg_private_step(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor],
         int(step), int(proj_step), ps.sample_norms.data_ptr(), ps.ws3.data_ptr(),
         ps.ws3_bytes, _stream_handle(stream)))
     return ps.G_priv, ps.sample_norms
+
+
+@_on_stream
+def dpg_rc_norms(A: Sequence[torch.Tensor], dY: Sequence[torch.Tensor], k: int,
+                 clip_C: float, seed: int, step: int,
+                 layer_ids: Optional[Sequence[int]] = None,
+                 norms: Optional[torch.Tensor] = None,
+                 scales: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """Randomized clipping's per-sample norm estimate (libdpg): Hutchinson's
+    estimator with k Gaussian probes per layer on the d_out side.
+    A[l]: [B, T, d_in_l], dY[l]: [B, T, d_out_l] (bf16 or fp32, on the GPU).
+    Returns (estimated norms [B], clip factors min(1, C / nhat) [B])."""
+    lib = load_library()
+    n = len(A)
+    if n < 1 or len(dY) != n:
+        raise ValueError("A and dY must be non-empty lists of equal length")
+    dt = A[0].dtype
+    B, T = int(A[0].shape[0]), int(A[0].shape[1])
+    ids = list(range(n)) if layer_ids is None else [int(x) for x in layer_ids]
+    dev = A[0].device
+    norms = torch.empty(B, dtype=torch.float32, device=dev) if norms is None else norms
+    scales = torch.empty(B, dtype=torch.float32, device=dev) if scales is None else scales
+    _require(norms, "norms", torch.float32, (B,))
+    _require(scales, "scales", torch.float32, (B,))
+    arr = (LayerGrad * n)()
+    for i in range(n):
+        _require(A[i], f"A[{i}]", dt)
+        _require(dY[i], f"dY[{i}]", dt)
+        if A[i].dim() != 3 or dY[i].dim() != 3 or \
+                tuple(A[i].shape[:2]) != (B, T) or tuple(dY[i].shape[:2]) != (B, T):
+            raise ValueError(f"layer {i}: A and dY must be [B, T, d] with common B, T")
+        arr[i].d_in, arr[i].d_out, arr[i].layer_id = int(A[i].shape[2]), int(dY[i].shape[2]), ids[i]
+        arr[i].A, arr[i].dY, arr[i].G_priv = _ptr(A[i]), _ptr(dY[i]), None
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.dpg_rc_norms_workspace_size(arr, n, B, T, int(k), _dtype_code(dt),
+                                                ctypes.byref(need)))
+    ws, ws_bytes = _workspace(need.value, dev, workspace)
+    _check(lib, lib.dpg_rc_norms(arr, n, B, T, int(k), _dtype_code(dt), float(clip_C),
+                                 int(seed), int(step), norms.data_ptr(), scales.data_ptr(),
+                                 ws.data_ptr(), ws_bytes, _stream_handle(stream)))
+    return norms, scales
 
 
 def static_scratch_bytes() -> int:

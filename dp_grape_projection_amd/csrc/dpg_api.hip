@@ -660,6 +660,10 @@ int check_clip_sigma(double clip_C, double sigma) {
   return DPG_OK;
 }
 
+// Probe stream tag of the randomized-clipping norm estimate (P uses 0, the
+// noise 1).
+constexpr uint32_t kTagProbe = 3;
+
 // The projection call. With ghat == nullptr: the whole batch step (norms,
 // clip, sum, noise into each layer's G_priv). With ghat: the streaming form
 // for one layer (its product tiles into ghat, its squared norms added into
@@ -667,21 +671,27 @@ int check_clip_sigma(double clip_C, double sigma) {
 // With upd (the one-call step): the final stage also runs Adam on G_priv,
 // and the back-projection follows, reading the P this call generated; the
 // U buffers live after the projection workspace.
+// With rc_scales (the randomized-clipping norm estimate, on layers whose A
+// and dY the caller has swapped, so that "P" holds the probes on the d_out
+// side): P is drawn from the probe stream, the call stops after the norms,
+// and the clip factors go to rc_scales; sigma and G_priv are unused.
 int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
                  int64_t T, int32_t r, int32_t dtype, double clip_C,
                  double sigma, uint64_t seed, uint64_t step,
                  uint64_t proj_step, float* sample_norms, void* workspace,
                  size_t workspace_bytes, void* stream, float* ghat,
-                 float* norm_sq, const StepUpdate* upd = nullptr) {
+                 float* norm_sq, const StepUpdate* upd = nullptr,
+                 float* rc_scales = nullptr) {
   const bool layer_mode = ghat != nullptr;
+  const bool rc = rc_scales != nullptr;
   int st = validate_proj_shapes(layers, n_layers, B, T, r, dtype);
   if (st) return st;
   for (int i = 0; i < n_layers; ++i)
-    if (!layers[i].A || !layers[i].dY || (!layer_mode && !layers[i].G_priv))
+    if (!layers[i].A || !layers[i].dY || (!layer_mode && !rc && !layers[i].G_priv))
       return fail(DPG_ERR_INVALID_ARG,
                   "NULL data pointer in layer index " + std::to_string(i));
   if (layer_mode && !norm_sq) return fail(DPG_ERR_INVALID_ARG, "norm_sq is NULL");
-  if (!layer_mode && (st = check_clip_sigma(clip_C, sigma))) return st;
+  if (!layer_mode && (st = check_clip_sigma(clip_C, rc ? 0.0 : sigma))) return st;
   if ((st = check_seed_steps(layer_mode ? 1 : step, proj_step))) return st;
   const ProjPlan p = plan_proj(layers, n_layers, B, T, r, dtype);
   std::vector<size_t> off_U;
@@ -708,6 +718,7 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       a.k0 = k0;
       a.k1 = k1;
       a.step_word = static_cast<uint32_t>(proj_step);
+      a.tag = rc ? kTagProbe : 0u;
       int blocks = 0;
       for (int l = l0; l < l1; ++l)
         blocks += fill_gen_p(a.L[l - l0], ws + p.off_P[l], layers[l].d_in,
@@ -805,7 +816,7 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // the large per-sample kernel copies dY rows with 16-byte transfers; the
   // streaming form (which also stores each sample's product) takes the
   // regular one
-  const bool hat_sum = p.hat_sum && !layer_mode;
+  const bool hat_sum = p.hat_sum && !layer_mode && !rc;
   bool samp_big = p.has_samp_big && !layer_mode;
   for (int l = 0; l < n_layers; ++l)
     if (!aligned(layers[l].dY, 16)) samp_big = false;
@@ -875,6 +886,15 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   if (layer_mode) {
     NormAccArgs a{norm_part, sp.n_slots, static_cast<int32_t>(B), norm_sq};
     return timed(K_CLIP, s, [&] { return launch_norm_acc(a, s); });
+  }
+  if (rc) {
+    ScaleArgs a;
+    a.norm_part = norm_part;
+    a.n_slots = sp.n_slots;
+    a.clip_C = static_cast<float>(clip_C);
+    a.scales = rc_scales;
+    a.norms_out = sample_norms;
+    return timed(K_SCALE, s, [&] { return launch_scale(a, static_cast<int>(B), s); });
   }
   // 4. per-sample norm and clip factor (needs every layer's partials); the
   //    sum pass does it itself when the groups are small
@@ -1054,6 +1074,49 @@ int dpg_private_step(const dpg_layer_grad* layers, const dpg_layer_param* params
   return private_step_impl(layers, params, n_layers, B, T, r, dtype, clip_C, sigma, lr,
                            beta1, beta2, eps, seed, step, proj_step, sample_norms,
                            workspace, workspace_bytes, stream);
+}
+
+namespace {
+// The estimate's layers with A and dY swapped: the projection kernels then
+// form dY_i Q^T (the probes on the d_out side) and the norm pass
+// ||(dY_i Q^T)^T A_i||^2 = ||A_i^T dY_i Q^T||^2.
+int rc_swapped(const dpg_layer_grad* layers, int32_t n_layers, std::vector<dpg_layer_grad>* out) {
+  if (!layers) return fail(DPG_ERR_INVALID_ARG, "layers is NULL");
+  if (n_layers < 1 || n_layers > (1 << 20))
+    return fail(DPG_ERR_INVALID_ARG, "n_layers must be in [1, 2^20]");
+  out->assign(layers, layers + n_layers);
+  for (auto& L : *out) {
+    std::swap(L.d_in, L.d_out);
+    std::swap(L.A, L.dY);
+    L.G_priv = nullptr;
+  }
+  return DPG_OK;
+}
+}  // namespace
+
+int dpg_rc_norms_workspace_size(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
+                                int64_t T, int32_t k, int32_t dtype, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(DPG_ERR_INVALID_ARG, "bytes is NULL");
+  std::vector<dpg_layer_grad> sw;
+  int st = rc_swapped(layers, n_layers, &sw);
+  if (st) return st;
+  if ((st = validate_proj_shapes(sw.data(), n_layers, B, T, k, dtype))) return st;
+  *bytes = plan_proj(sw.data(), n_layers, B, T, k, dtype).total;
+  return DPG_OK;
+}
+
+int dpg_rc_norms(const dpg_layer_grad* layers, int32_t n_layers, int64_t B, int64_t T,
+                 int32_t k, int32_t dtype, double clip_C, uint64_t seed, uint64_t step,
+                 float* norms, float* scales, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  g_last_error.clear();
+  if (!norms || !scales) return fail(DPG_ERR_INVALID_ARG, "norms and scales must not be NULL");
+  std::vector<dpg_layer_grad> sw;
+  const int st = rc_swapped(layers, n_layers, &sw);
+  if (st) return st;
+  return project_impl(sw.data(), n_layers, B, T, k, dtype, clip_C, 0.0, seed, step, step, norms,
+                      workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, scales);
 }
 
 int dpg_project_layer_workspace_size(const dpg_layer_grad* layer, int64_t B,

@@ -54,6 +54,7 @@ struct GenPArgs {
   int32_t r;
   float scale;        // 1 / sqrt(r)
   uint32_t k0, k1, step_word;
+  uint32_t tag;       // stream tag: 0 for P, 3 for norm-estimate probes
 };
 
 // ---- Xt = P A^T over a K range; written per sample as Xt[b][j][t] (row

@@ -112,7 +112,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void gen_p_kernel(const GenPArgs a) {
   const int b = blockIdx.x;
   const GenPLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
-  const StreamKey key{a.k0, a.k1, a.step_word, 0u};
+  const StreamKey key{a.k0, a.k1, a.step_word, a.tag};
   gen_p_thread<T>(L, (b - L.block0) * kThreads + static_cast<int>(threadIdx.x),
                   a.r, a.scale, key);
 }

@@ -285,6 +285,43 @@ int dpg_clip_sum_noise(const dpg_layer_hat* layers, int32_t n_layers,
                        size_t workspace_bytes, void* stream);
 
 /*
+ * dpg_rc_norms_workspace_size / dpg_rc_norms: per-sample gradient norms
+ * estimated without forming them, the norm-estimation routine of randomized
+ * clipping ("DP-SGD Eficiente para LLMs con Recorte Aleatorizado",
+ * gist.science technical summary: Methodology DP-SGD-RC, core mechanism -
+ * the trace identity and Hutchinson's estimator; Algorithmic flow, steps 3
+ * and 4). For every sample i:
+ *     nhat_i^2 = sum_l (1/k) sum_j || A_il^T (dY_il q_lj) ||^2
+ *   an unbiased estimate of sum_l ||A_il^T dY_il||_F^2 = sum_l tr(O_il),
+ *   O_il = dY_il^T A_il A_il^T dY_il, from k probes q_lj per layer with
+ *   i.i.d. standard normal entries on O's side (d_out):
+ *   q_lj[c] = z(seed, layer_id, step, tag 3, e = j*d_out + c), z as above;
+ *     s_i = min(1, C / nhat_i)   (s_i = 1 when nhat_i = 0 or C = +inf).
+ *   The work is two contractions per layer, dY_i Q^T [T][k] and then
+ *   A_i^T (dY_i Q^T) [d_in][k] reduced to its squared norm, O(B T k (d_in +
+ *   d_out)) flops; A and dY are read once each.
+ * Arguments:
+ *   layers, n_layers  as for dpg_project_clip_noise; G_priv is not used
+ *   B, T, dtype       as for dpg_project_clip_noise
+ *   k                 probes per layer (>= 1); k*d_in and k*d_out <= 2^31 - 8
+ *   clip_C            clip threshold C > 0, or +INFINITY
+ *   seed, step        key the probes (1 <= step < 2^32): a fresh draw per step
+ *   norms, scales     device out [B] fp32: nhat_i and s_i
+ *   workspace         device scratch of at least
+ *                     dpg_rc_norms_workspace_size(...) bytes, 256-byte aligned
+ *   stream            hipStream_t to enqueue on
+ * Errors as for every entry point (shapes, NULL pointers, workspace) before
+ * anything is enqueued.
+ */
+int dpg_rc_norms_workspace_size(const dpg_layer_grad* layers, int32_t n_layers,
+                                int64_t B, int64_t T, int32_t k, int32_t dtype,
+                                size_t* bytes);
+int dpg_rc_norms(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
+                 int64_t T, int32_t k, int32_t dtype, double clip_C,
+                 uint64_t seed, uint64_t step, float* norms, float* scales,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dpg_philox_normals: the random stream both calls draw from, exposed so it
  * can be checked on its own. For e in [start, start + n):
  *     z_out[e - start] = z(seed, layer_id, step_word, tag, e)
