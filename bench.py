@@ -59,6 +59,9 @@ def parse():
                          "the default for enc12, dec24 and long1, whose host "
                          "draws would take minutes. The CPU oracle then runs on "
                          "one block at two batch sizes and is extrapolated.")
+    ap.add_argument("--rc-k", type=int, default=32,
+                    help="probes per layer of the randomized-clipping norm "
+                         "estimate timed beside the step (0: skip it)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the steps, copy a buffer of this many MiB "
                          "three times (calibrates HBM byte counters)")
@@ -407,6 +410,50 @@ def main():
               file=sys.stderr, flush=True)
         del sprep
 
+    # Randomized clipping's per-sample norm estimate (dpg_rc_norms) on the
+    # same inputs: k probes per layer; its algorithmic bytes are A and dY
+    # read once each plus the probes, its flops 2 B T k (d_in + d_out).
+    rc = None
+    if args.rc_k > 0:
+        ids = [L.layer_id for L in wl.layers]
+        es = 2 if wl.dtype == "bf16" else 4
+        for _ in range(3):
+            step += 1
+            dpg.dpg_rc_norms(A, dY, k=args.rc_k, clip_C=wl.clip_C, seed=wl.seed, step=step,
+                             layer_ids=ids)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step += 1
+            dpg.dpg_rc_norms(A, dY, k=args.rc_k, clip_C=wl.clip_C, seed=wl.seed, step=step,
+                             layer_ids=ids)
+        e1.record()
+        torch.cuda.synchronize()
+        rc_ms = e0.elapsed_time(e1) / args.steps
+        dpg.timing_read(reset=True)
+        dpg.timing_enable(True)
+        for _ in range(3):
+            step += 1
+            dpg.dpg_rc_norms(A, dY, k=args.rc_k, clip_C=wl.clip_C, seed=wl.seed, step=step,
+                             layer_ids=ids)
+        torch.cuda.synchronize()
+        rc_times = dpg.timing_read(reset=True)
+        dpg.timing_enable(False)
+        rc_bytes = sum(wl.B * wl.T * (L.d_in + L.d_out) * es + args.rc_k * L.d_out * es
+                       for L in wl.layers)
+        rc_flops = sum(2.0 * wl.B * wl.T * args.rc_k * (L.d_in + L.d_out) for L in wl.layers)
+        rc = {"k": args.rc_k, "ms_per_call": round(rc_ms, 5),
+              "samples_per_s": round(wl.B / (rc_ms * 1e-3), 1),
+              "algorithmic_bytes": int(rc_bytes), "algorithmic_flops": rc_flops,
+              "hbm_GB/s": round(rc_bytes / (rc_ms * 1e-3) / 1e9, 1),
+              "bound": "hbm", "frac": round(rc_bytes / (rc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+              "kernels_us_per_call": {k: round(ms * 1e3 / 3, 2)
+                                      for k, (ms, n) in rc_times.items() if n > 0}}
+        print(f"[bench] rc_norms (k={args.rc_k}): {rc_ms * 1e3:.1f} us/call",
+              file=sys.stderr, flush=True)
+
     if args.copy_mb > 0:
         n = args.copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -445,6 +492,7 @@ def main():
         "cpu_baseline": cpu,
         "two_call": two_call,
         "streaming": streaming,
+        "rc_norms": rc,
     }
     print(json.dumps(out), flush=True)
 
