@@ -356,3 +356,45 @@ def test_static_step_rejects_a_step_beyond_its_scratch(lib):
     bad = list(args)
     bad[5] = 0   # r = 0
     assert lib.dpg_private_step_static(*bad) == dpg.binding.DPG_ERR_INVALID_ARG
+
+
+BAD_RC = [
+    ("zero batch", dict(B=0)),
+    ("zero k", dict(k=0)),
+    ("bad dtype", dict(dtype=7)),
+    ("zero C", dict(C=0.0)),
+    ("NaN C", dict(C=float("nan"))),
+    ("step 0", dict(step=0)),
+    ("step 2^32", dict(step=2 ** 32)),
+    ("duplicate ids", dict(ids=[3, 3])),
+    ("k*d_out 2^31", dict(shapes=[(4, 2 ** 22), (4, 4)], k=512)),
+    ("null data", dict(ptr=0)),
+    ("null norms", dict(norms=None)),
+]
+
+
+@pytest.mark.parametrize("desc,kw", BAD_RC, ids=[d for d, _ in BAD_RC])
+def test_rc_norms_rejects_invalid_arguments(lib, desc, kw):
+    """dpg_rc_norms validates before it enqueues anything (no GPU needed)."""
+    shapes = kw.get("shapes", [(16, 8), (8, 16)])
+    arr = _grads(shapes, kw.get("ids"), kw.get("ptr", 0x1000))
+    st = lib.dpg_rc_norms(arr, len(shapes), kw.get("B", 2), kw.get("T", 3), kw.get("k", 4),
+                          kw.get("dtype", 1), kw.get("C", 1.0), 0, kw.get("step", 1),
+                          kw.get("norms", 0x20000), 0x30000, 0x10000, 1 << 30, None)
+    assert st == dpg.binding.DPG_ERR_INVALID_ARG, desc
+    assert lib.dpg_last_error() != b""
+
+
+def test_rc_norms_workspace(lib):
+    """The estimate's workspace query: positive and 256-aligned for valid
+    shapes, growing with k; a short workspace is rejected."""
+    arr = _grads([(768, 3072), (3072, 768)])
+    small, big = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.dpg_rc_norms_workspace_size(arr, 2, 32, 128, 8, 1, ctypes.byref(small)) == 0
+    assert lib.dpg_rc_norms_workspace_size(arr, 2, 32, 128, 64, 1, ctypes.byref(big)) == 0
+    assert 0 < small.value < big.value and big.value % 256 == 0
+    assert lib.dpg_rc_norms_workspace_size(arr, 2, 32, 128, 8, 1, None) == \
+        dpg.binding.DPG_ERR_INVALID_ARG
+    st = lib.dpg_rc_norms(arr, 2, 32, 128, 8, 1, 1.0, 0, 1, 0x20000, 0x30000, 0x10000,
+                          small.value - 1, None)
+    assert st == dpg.binding.DPG_ERR_WORKSPACE
