@@ -319,8 +319,9 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char* __restrict__ p) {
 }
 __device__ __forceinline__ float lds_read_f32(const float* __restrict__ p) { return *p; }
 
-// BK: K step (elements). Two stages; rows of a stage are BK * 2 bytes in CH
-// chunks of 16 bytes; chunk c of row R sits in slot c ^ (R / 2 mod CH).
+// BK: K step (elements). Two stages of P and three of A; rows of a stage
+// are BK * 2 bytes in CH chunks of 16 bytes; chunk c of row R sits in slot
+// c ^ (R / 2 mod CH).
 //
 // Matrix-core schedule: a wave's fragments are double-buffered over the K
 // sub-steps of 16 and across steps. In each sub-step the wave issues one
@@ -329,8 +330,9 @@ __device__ __forceinline__ float lds_read_f32(const float* __restrict__ p) { ret
 // seven MFMAs, so LDS latency hides behind matrix-core work. In the last
 // sub-step of step s, after four MFMAs, every wave has read all of step s:
 // it waits for its copies of step s + 1, meets the others at the barrier,
-// refills the stage of step s with step s + 2 and reads the first fragments
-// of step s + 1 while the remaining four MFMAs run.
+// refills P's stage of step s with step s + 2 and A's with step s + 3, and
+// reads the first fragments of step s + 1 while the remaining four MFMAs
+// run.
 template <int BK>
 __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArgs a) {
   constexpr int kRowBytes = BK * 2;
@@ -339,11 +341,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   constexpr int kCopiesPerTile = kBigM / kRowsPerCopy;
   constexpr int kCopiesPerWave = 2 * kCopiesPerTile / 8;  // per step
   constexpr int kTileBytes = kBigM * kRowBytes;
-  constexpr int kStageBytes = 2 * kTileBytes;
   constexpr int KK = BK / 16;                         // sub-steps per step
   static_assert(kBigM == kBigN && BK % 16 == 0 && (CH & (CH - 1)) == 0 && KK >= 2, "tile shape");
   static_assert(kCopiesPerWave * 8 == 2 * kCopiesPerTile, "copies per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  // Three stages of the A tile (the operand streamed from HBM, whose copies
+  // run two steps ahead of their use) and two of P (L2-resident): 160 KiB.
+  constexpr int NA = 3;
+  constexpr int kCopiesA = kCopiesPerWave / 2;       // per wave and step, of each operand
+  __shared__ __attribute__((aligned(1024))) char smem[(2 + NA) * kTileBytes];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
   const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
@@ -379,19 +384,25 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   const uint32_t chunk = static_cast<uint32_t>(((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) << 4);
   const uint32_t voffP = static_cast<uint32_t>(lane >> 3) * p_rb + chunk;
   const uint32_t voffA = static_cast<uint32_t>(lane >> 3) * a_rb + chunk;
-  auto issue = [&](int step, int stage) {
-    char* sb = smem + stage * kStageBytes;
+  // P stage q at q * kTileBytes (q < 2), A stage q at (2 + q) * kTileBytes
+  auto issue_p = [&](int step, int stage) {
+    char* sb = smem + stage * kTileBytes;
     const uint32_t kb = static_cast<uint32_t>(s_begin + step) * kRowBytes;
 #pragma unroll
-    for (int q = 0; q < kCopiesPerWave; ++q) {
-      const int g = q * 8 + wave;
-      const bool is_a = g >= kCopiesPerTile;
-      const int gi = is_a ? g - kCopiesPerTile : g;
-      const uint32_t row0 = static_cast<uint32_t>((is_a ? n0 : j0) + gi * kRowsPerCopy);
-      if (is_a)
-        copy_to_lds(rsA, voffA, row0 * a_rb + kb, sb + kTileBytes + gi * 1024);
-      else
-        copy_to_lds(rsP, voffP, row0 * p_rb + kb, sb + gi * 1024);
+    for (int q = 0; q < kCopiesA; ++q) {
+      const int gi = q * 8 + wave;
+      const uint32_t row0 = static_cast<uint32_t>(j0 + gi * kRowsPerCopy);
+      copy_to_lds(rsP, voffP, row0 * p_rb + kb, sb + gi * 1024);
+    }
+  };
+  auto issue_a = [&](int step, int stage) {
+    char* sb = smem + (2 + stage) * kTileBytes;
+    const uint32_t kb = static_cast<uint32_t>(s_begin + step) * kRowBytes;
+#pragma unroll
+    for (int q = 0; q < kCopiesA; ++q) {
+      const int gi = q * 8 + wave;
+      const uint32_t row0 = static_cast<uint32_t>(n0 + gi * kRowsPerCopy);
+      copy_to_lds(rsA, voffA, row0 * a_rb + kb, sb + gi * 1024);
     }
   };
 
@@ -400,9 +411,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   const int r32 = lane & 31, kh = lane >> 5;
   // fragments of sub-step kk of the step in stage `stage`: this lane's
   // 16-byte chunk is k = 16 kk + 8 kh
-  auto read_frags = [&](int stage, int kk, bf16x8* af, bf16x8* bfr) {
-    const char* sP = smem + stage * kStageBytes;
-    const char* sA = sP + kTileBytes;
+  auto read_frags = [&](int step, int kk, bf16x8* af, bf16x8* bfr) {
+    const char* sP = smem + (step & 1) * kTileBytes;
+    const char* sA = smem + (2 + step % NA) * kTileBytes;
     const int c = 2 * kk + kh;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -424,12 +435,23 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
             af[q >> 1], bfr[q & 1], acc.v[q >> 1][q & 1], 0, 0, 0);
   };
 
+  // Copies in issue order: P and A of step 0; P of step 1, A of steps 1 ..
+  // NA - 1; then at the barrier ending step s, P of step s + 2 and A of
+  // step s + NA. So before that barrier, step s + 1's copies are complete
+  // once at most the A copies of step s + 2 (NA = 3) are still in flight:
+  // loads return in order.
   bf16x8 fa[2][4], fb[2][2];
+  int a_stage = 0;  // the A stage of step s: s mod NA
   if (n_steps > 0) {
-    issue(0, 0);
+    issue_p(0, 0);
+    issue_a(0, 0);
     wait_vm(0);
     lds_barrier();
-    if (n_steps > 1) issue(1, 1);
+    if (n_steps > 1) {
+      issue_p(1, 1);
+      issue_a(1, 1);
+    }
+    if (n_steps > 2) issue_a(2, 2);
     read_frags(0, 0, fa[0], fb[0]);
   }
   for (int s = 0; s < n_steps; ++s) {
@@ -441,18 +463,22 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
       mma(fa[cur], fb[cur], 0, first);
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < KK) {
-        read_frags(s & 1, kk + 1, fa[nxt], fb[nxt]);
+        read_frags(s, kk + 1, fa[nxt], fb[nxt]);
       } else if (s + 1 < n_steps) {
-        wait_lgkm0();  // this wave's reads of stage s & 1 are complete
-        wait_vm(0);    // its copies of step s + 1 landed
+        wait_lgkm0();  // this wave's reads of step s's stages are complete
+        // its copies of step s + 1 landed
+        if (s + 2 < n_steps) wait_vm(kCopiesA);
+        else wait_vm(0);
         lds_barrier();
-        if (s + 2 < n_steps) issue(s + 2, s & 1);
-        read_frags((s + 1) & 1, 0, fa[nxt], fb[nxt]);
+        if (s + 2 < n_steps) issue_p(s + 2, s & 1);
+        if (s + NA < n_steps) issue_a(s + NA, a_stage);
+        read_frags(s + 1, 0, fa[nxt], fb[nxt]);
       }
       __builtin_amdgcn_sched_barrier(0);
       mma(fa[cur], fb[cur], first, 8);
       __builtin_amdgcn_sched_barrier(0);
     }
+    a_stage = a_stage + 1 == NA ? 0 : a_stage + 1;
   }
 
   // lane: column n0 + 64 wn + 32 nb + r32; registers i: rows
