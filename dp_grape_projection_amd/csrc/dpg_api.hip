@@ -3,7 +3,9 @@
 // is allocated here and no state survives a call (apart from the calling
 // thread's last error message).
 #include <algorithm>
-#include <map>
+#include <functional>
+#include <queue>
+#include <set>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -219,8 +221,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   const int64_t steps_per_block = std::max<int64_t>(1, ceil_div(units, target / 2));
   // Large bf16 projections run in 256 x 256 tiles with K steps of 64, one
   // 8-wave block per CU. The K steps per block minimise an estimate of the
-  // time in steps, max(work / CUs, longest block), plus the split partials
-  // (written and read back) at the bytes one step moves per CU.
+  // time in steps (per launch, below) plus the split partials.
   // (its epilogue stores use 32-bit offsets: all of Xt, and 256 rows of a
   // split partial)
   p.big = dtype == DPG_BF16 && r % kBigM == 0 && BT % kBigN == 0 && BT >= 2 * kBigN &&
@@ -236,32 +237,71 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   int64_t big_sps = 0;
   if (p.big) {
     const int64_t tiles = (r / kBigM) * (BT / kBigN), cus = target / 2;
-    int64_t work = 0, max_steps = 1;
-    std::map<int64_t, int64_t> n_of_steps;  // K steps of a layer -> layers
-    for (int l = 0; l < n_layers; ++l) {
-      work += tiles * (layers[l].d_in / kBigK);
+    int64_t max_steps = 1;
+    for (int l = 0; l < n_layers; ++l)
       max_steps = std::max<int64_t>(max_steps, layers[l].d_in / kBigK);
-      ++n_of_steps[layers[l].d_in / kBigK];
-    }
-    // candidates: the K steps per block that split the longest layer into
-    // 1, 2, ... (at most 1024) parts, longest first
-    double best = -1.0;
-    int64_t prev = -1;
-    for (int64_t parts = 1; parts <= std::min<int64_t>(max_steps, 1024); ++parts) {
-      const int64_t sps = ceil_div(max_steps, parts);
-      if (sps == prev) continue;
-      prev = sps;
-      int64_t blocks = 0, longest = 0;
-      double part = 0.0;
-      for (const auto& kv : n_of_steps) {
-        const int64_t steps = kv.first, sp = ceil_div(steps, sps);
-        blocks += tiles * sp * kv.second;
-        longest = std::max<int64_t>(longest, ceil_div(steps, sp));
-        if (sp > 1) part += 2.0 * sp * r * BT * 4 * kv.second;
+    // Candidates: the K steps per block that split the longest layer into
+    // 1, 2, ... (at most 1024) parts, and any layer into 1 to 4 parts.
+    std::set<int64_t> cand;
+    for (int64_t parts = 1; parts <= std::min<int64_t>(max_steps, 1024); ++parts)
+      cand.insert(ceil_div(max_steps, parts));
+    for (int l = 0; l < n_layers; ++l)
+      for (int64_t parts = 1; parts <= 4; ++parts)
+        cand.insert(ceil_div(layers[l].d_in / kBigK, parts));
+    // Time of one launch in K steps. A launch of at most 4 rounds of
+    // resident blocks is simulated as the hardware runs it: each XCD takes a
+    // contiguous range of the logical blocks (xcd_logical_block) in order,
+    // one block per CU as CUs free up, so blocks of unequal lengths can
+    // leave a long tail; a longer launch is estimated as max(work / CUs,
+    // longest block).
+    auto launch_steps = [&](int l0, int l1, int64_t sps) {
+      std::vector<int64_t> lens;
+      int64_t work = 0, longest = 0;
+      for (int l = l0; l < l1; ++l) {
+        const int64_t steps = layers[l].d_in / kBigK, sp = ceil_div(steps, sps),
+                      per = ceil_div(steps, sp);
+        work += tiles * steps;
+        longest = std::max(longest, per);
+        if (static_cast<int64_t>(lens.size()) <= 4 * cus)
+          for (int64_t k = 0; k < sp; ++k)
+            lens.insert(lens.end(), tiles, std::min(per, steps - k * per));
       }
-      const double t = static_cast<double>(blocks <= cus ? longest
-                                                         : std::max(ceil_div(work, cus), longest)) +
-                       part / (static_cast<double>(kBigM + kBigN) * kBigK * 2 * cus);
+      const int64_t blocks = static_cast<int64_t>(lens.size());
+      if (blocks > 4 * cus) return std::max(ceil_div(work, cus), longest);
+      const int64_t per_xcd = ceil_div(blocks, 8), slots = cus / 8;
+      int64_t span = 0;
+      for (int64_t x = 0; x < 8; ++x) {
+        // the CUs' finish times; the next block goes to the earliest
+        std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> busy(
+            std::greater<int64_t>(), std::vector<int64_t>(slots, 0));
+        int64_t end = 0;
+        for (int64_t b = x * per_xcd; b < std::min(blocks, (x + 1) * per_xcd); ++b) {
+          const int64_t t = busy.top() + lens[b];
+          busy.pop();
+          busy.push(t);
+          end = std::max(end, t);
+        }
+        span = std::max(span, end);
+      }
+      return span;
+    };
+    double best = -1.0;
+    for (auto it = cand.rbegin(); it != cand.rend(); ++it) {  // longest first
+      const int64_t sps = *it;
+      double part = 0.0;
+      int64_t steps_total = 0;
+      for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers)
+        steps_total += launch_steps(l0, std::min(n_layers, l0 + kMaxLayers), sps);
+      for (int l = 0; l < n_layers; ++l) {
+        const int64_t sp = ceil_div(layers[l].d_in / kBigK, sps);
+        if (sp > 1) part += 2.0 * sp * r * BT * 4;
+      }
+      // the split partials (written, then read back by the xsum launch),
+      // counted at a third of the bytes a K step moves per CU: measured,
+      // a split of dec24's 8192-wide layers cost about three times what
+      // their bytes at that rate predict
+      const double t = static_cast<double>(steps_total) +
+                       3.0 * part / (static_cast<double>(kBigM + kBigN) * kBigK * 2 * cus);
       if (best < 0.0 || t < best) {
         best = t;
         big_sps = sps;
