@@ -57,14 +57,13 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1,
                                               uint32_t out[4]) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t lo0 = c0 * 0xD2511F53u;
-    const uint32_t hi0 = __umulhi(c0, 0xD2511F53u);
-    const uint32_t lo1 = c2 * 0xCD9E8D57u;
-    const uint32_t hi1 = __umulhi(c2, 0xCD9E8D57u);
-    c0 = hi1 ^ c1 ^ k0;
-    c1 = lo1;
-    c2 = hi0 ^ c3 ^ k1;
-    c3 = lo0;
+    // one 32x32 -> 64-bit multiply gives both halves
+    const uint64_t p0 = static_cast<uint64_t>(c0) * 0xD2511F53u;
+    const uint64_t p1 = static_cast<uint64_t>(c2) * 0xCD9E8D57u;
+    c0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+    c1 = static_cast<uint32_t>(p1);
+    c2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    c3 = static_cast<uint32_t>(p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -86,6 +85,19 @@ __device__ __forceinline__ float uniform_open01(uint32_t x) {
 // tails: there an ulp of z is 4.8e-7.) On gfx950 float64 adds and
 // multiply-adds issue at the rate of non-packed fp32 ones.
 
+// 1 / d for d in [1.7, 2.5], and 1 / sqrt(x) for a normal x > 0: the fp32
+// hardware approximation (relative error about 2^-23), then one Newton-
+// Raphson step in float64, y <- y (2 - d y) and y <- y (3 - x y^2) / 2,
+// which squares the relative error (below 1e-13).
+__device__ __forceinline__ double recip_mid(double d) {
+  const double y = static_cast<double>(__builtin_amdgcn_rcpf(static_cast<float>(d)));
+  return fma(y, fma(-d, y, 1.0), y);
+}
+__device__ __forceinline__ double rsqrt_pos(double x) {
+  const double y = static_cast<double>(__builtin_amdgcn_rsqf(static_cast<float>(x)));
+  return fma(0.5 * y, fma(-x * y, y, 1.0), y);
+}
+
 // ln u for u in (0, 1) (a normal double): u = m 2^e with m in [1/sqrt 2,
 // sqrt 2), and ln m = 2 atanh(s) with s = (m - 1) / (m + 1), |s| <= 0.1716,
 // from the odd series atanh(s) = s (1 + s^2/3 + s^4/5 + ...) cut after the
@@ -97,7 +109,7 @@ __device__ __forceinline__ double ln_unit(double u) {
     m *= 2.0;
     e -= 1;
   }
-  const double s = (m - 1.0) / (m + 1.0);
+  const double s = (m - 1.0) * recip_mid(m + 1.0);
   const double s2 = s * s;
   double p = 1.0 / 11.0;
   p = fma(p, s2, 1.0 / 9.0);
@@ -146,7 +158,8 @@ __device__ __forceinline__ void box_muller4(const uint32_t w[4], float z[4]) {
   for (int h = 0; h < 2; ++h) {
     const double u = static_cast<double>(uniform_open01(w[2 * h]));
     const double t = static_cast<double>(uniform_open01(w[2 * h + 1]));
-    const double R = __builtin_sqrt(-2.0 * ln_unit(u));
+    const double x = -2.0 * ln_unit(u);  // in [1.1e-7, 33.3]
+    const double R = x * rsqrt_pos(x);
     double c, s;
     cossin_turns(t, c, s);
     z[2 * h] = static_cast<float>(R * c);
