@@ -10,6 +10,7 @@
 namespace dpg {
 
 constexpr int kThreads = 256;  // every kernel: 4 wavefronts of 64 lanes
+constexpr int kScaleThreads = 1024;  // (but the per-sample norm kernel: 16)
 constexpr int kMaxLayers = 32;
 
 // Matrix-core tiles: 128 x 128 outputs per block; the K step is 128 for

@@ -1062,14 +1062,28 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
 
 // ------------------------------------------------------------------ scale --
 
-__global__ __launch_bounds__(kThreads) void scale_kernel(const ScaleArgs a) {
-  __shared__ float red4[4];
-  const int i = blockIdx.x;
+__global__ __launch_bounds__(kScaleThreads) void scale_kernel(const ScaleArgs a) {
+  // one block per sample; thread t adds the 16-byte groups t, t + 1024,
+  // ... of the sample's slots (n_slots is a multiple of 4: every tiling
+  // writes 4 or 8 partials per tile), then a fixed-order reduction
+  __shared__ float red[kScaleThreads / 64];
+  const int i = blockIdx.x, tid = threadIdx.x;
   const float* p = a.norm_part + static_cast<int64_t>(i) * a.n_slots;
   float s = 0.0f;
-  for (int k = threadIdx.x; k < a.n_slots; k += kThreads) s += p[k];
-  const float tot = block_sum(s, red4);
-  if (threadIdx.x == 0) {
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(p);
+  const int n4 = a.n_slots >> 2;
+#pragma unroll 4
+  for (int k = tid; k < n4; k += kScaleThreads) {
+    const f32x4 v = p4[k];
+    s += (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  s = wave_sum(s);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kScaleThreads / 64; ++w) tot += red[w];
     const float n = sqrtf(tot);
     a.scales[i] = (n > a.clip_C) ? a.clip_C / n : 1.0f;
     if (a.norms_out) a.norms_out[i] = n;
@@ -1751,7 +1765,7 @@ hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
 }
 
 hipError_t launch_scale(const ScaleArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL(scale_kernel, dim3(B), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(scale_kernel, dim3(B), dim3(kScaleThreads), 0, s, a);
   return hipGetLastError();
 }
 
