@@ -1559,11 +1559,22 @@ __global__ __launch_bounds__(kThreads, 2) void back_big_kernel(const BackArgs a)
       }
   };
 
-  // vmcnt(n) for the copy counts below (6 copies a wave and step)
-  auto wait_copies = [](int n) {
-    if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
-    else if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F76);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  // vmcnt(n) for the counts below (6 copies a wave and step, 32 loads a
+  // W block): vmcnt's low four bits sit in bits 3:0 of the operand, its
+  // high two in bits 15:14; a count above 63 waits for 63
+  auto wait_ops = [](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+      case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+      case 32: __builtin_amdgcn_s_waitcnt(0x8F70); break;
+      case 38: __builtin_amdgcn_s_waitcnt(0x8F76); break;
+      case 44: __builtin_amdgcn_s_waitcnt(0x8F7C); break;
+      default:
+        if (n > 63) __builtin_amdgcn_s_waitcnt(0xCF7F);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);  // (stricter: wait for all)
+        break;
+    }
   };
   constexpr int kCopies = kCopiesP + kCopiesU;
   acc.zero();
@@ -1572,15 +1583,21 @@ __global__ __launch_bounds__(kThreads, 2) void back_big_kernel(const BackArgs a)
 #pragma unroll
     for (int q = 0; q < NS; ++q)
       if (q < n_steps) issue(q, q);
-    wait_copies((min(NS, n_steps) - 1) * kCopies);
+    wait_ops((min(NS, n_steps) - 1) * kCopies);
     lds_barrier();
   }
   WBlock w0, w1;
   int stage = 0;
+  // A tile's W: rows 0-31 (block 0) are loaded at the start of its
+  // second-last K step, rows 32-63 at the start of its last, the other two
+  // blocks after its product is complete; each block is stored as soon as
+  // its loads are in, the next block's loads in flight meanwhile.
   for (int s = 0; s < n_steps; ++s) {
-    const bool last = s % kr == kr - 1;
+    const int ks = s % kr;
+    const bool last = ks == kr - 1;
     const int nt = nt0 + s / kr;
-    if (last) load_w(nt, 0, w0);
+    if (ks == kr - 2 || (kr == 1 && last)) load_w(nt, 0, w0);
+    if (kr >= 2 && last) load_w(nt, 1, w1);
     const char* sP = smem + stage * kStage;
     const char* sU = sP + kTileP;
 #pragma unroll
@@ -1599,19 +1616,23 @@ __global__ __launch_bounds__(kThreads, 2) void back_big_kernel(const BackArgs a)
     }
     if (s + 1 < n_steps) {
       wait_lgkm0();  // this wave's reads of stage `stage` are complete
-      // its copies of step s + 1 landed: loads return in order, so the
-      // copies issued after them (steps s + 2 .. s + NS - 1) may stay in
-      // flight, unless W stores are outstanding too (the previous step ended
-      // a tile): stores may complete out of order, so then wait for all
+      // its copies of step s + 1 landed: loads return in order, so what
+      // was issued after them may stay in flight: the copies of steps
+      // s + 2 .. s + NS - 1 and the W loads of this step and the one before
+      // (64 of them in a tile's last step, so a wait for 63 there: the
+      // first 7 of block 0's loads, a step old, complete as well); unless
+      // W stores are outstanding too (the previous step ended a tile):
+      // stores may complete out of order, so then wait for all
+      const int w_after = (kr >= 2 && last) ? 64 : (ks == kr - 2 || (kr == 1 && last)) ? 32 : 0;
       if (s % kr == 0 && s > 0) wait_vm(0);
-      else wait_copies((min(s + NS - 1, n_steps - 1) - (s + 1)) * kCopies);
+      else wait_ops((min(s + NS - 1, n_steps - 1) - (s + 1)) * kCopies + w_after);
       lds_barrier();
       // every wave has read stage `stage`: it takes step s + NS
       if (s + NS < n_steps) issue(s + NS, stage);
     }
     stage = stage + 1 == NS ? 0 : stage + 1;
     if (last) {
-      load_w(nt, 1, w1);
+      if (kr == 1) load_w(nt, 1, w1);
       store_w(nt, 0, w0);
       load_w(nt, 2, w0);
       store_w(nt, 1, w1);
