@@ -1,7 +1,10 @@
 // Launch descriptors shared by the host side of the C ABI (dpg_api.hip) and
 // the kernels (dpg_kernels.hip). Layer tables travel as kernel arguments, up
 // to kMaxLayers layers per launch; larger calls are split into several
-// launches.
+// launches. Beside its layer table, each argument block carries the layers'
+// first blocks as one contiguous array (first_block), which the launch
+// functions fill from the table: a block finds its layer from that array
+// with a few wide scalar loads, all in flight together.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,7 +14,8 @@ namespace dpg {
 
 constexpr int kThreads = 256;  // every kernel: 4 wavefronts of 64 lanes
 constexpr int kScaleThreads = 1024;  // (but the per-sample norm kernel: 16)
-constexpr int kMaxLayers = 32;
+constexpr int kMaxLayers = 48;
+static_assert(kMaxLayers >= 16, "the layer lookup scans 16 entries first");
 
 // Matrix-core tiles: 128 x 128 outputs per block; the K step is 128 for
 // bf16 operands and 32 for fp32 operands.
@@ -51,6 +55,7 @@ struct GenPLayer {
 };
 struct GenPArgs {
   GenPLayer L[kMaxLayers];
+  int32_t first_block[kMaxLayers];  // L[i].block0; INT32_MAX past n_layers
   int32_t n_layers;
   int32_t r;
   float scale;        // 1 / sqrt(r)
@@ -77,6 +82,7 @@ struct ProjLayer {
 };
 struct ProjArgs {
   ProjLayer L[kMaxLayers];
+  int32_t first_block[kMaxLayers];  // L[i].block0; INT32_MAX past n_layers
   int32_t n_layers;
   int32_t n_blocks;   // logical blocks (grid is rounded up to a multiple of 8)
   int32_t B, T, r, ldt;
@@ -94,6 +100,7 @@ struct XsumLayer {
 };
 struct XsumArgs {
   XsumLayer L[kMaxLayers];
+  int32_t first_block[kMaxLayers];  // L[i].block0; INT32_MAX past n_layers
   int32_t n_layers;
   int32_t B, T, r, ldt;
 };
@@ -115,6 +122,7 @@ struct SampLayer {
 };
 struct SampArgs {
   SampLayer L[kMaxLayers];
+  int32_t first_block[kMaxLayers];  // L[i].block0; INT32_MAX past n_layers
   int32_t n_layers;
   int32_t n_blocks;
   int32_t B, T, r, ldt;
@@ -175,6 +183,7 @@ struct FinLayer {
 };
 struct FinArgs {
   FinLayer L[kMaxLayers];
+  int32_t first_block[kMaxLayers];  // L[i].block0; INT32_MAX past n_layers
   const float* weights;  // [groups] or null (streaming form: the clip factors)
   int32_t n_layers;
   int32_t groups;
@@ -198,6 +207,8 @@ struct AdamLayer {
 struct PrepArgs {
   AdamLayer A[kMaxLayers];
   GenPLayer P[kMaxLayers];
+  int32_t first_a[kMaxLayers];  // A[i].block0; INT32_MAX past n_layers
+  int32_t first_p[kMaxLayers];  // P[i].block0; INT32_MAX past n_layers
   int32_t n_layers;
   int32_t adam_blocks;  // blocks [0, adam_blocks) run Adam, the rest gen P
   int32_t r;
@@ -220,6 +231,7 @@ struct BackLayer {
 };
 struct BackArgs {
   BackLayer L[kMaxLayers];
+  int32_t first_block[kMaxLayers];  // L[i].block0; INT32_MAX past n_layers
   int32_t n_layers;
   int32_t n_blocks;
   int32_t r;
@@ -238,25 +250,31 @@ struct BackArgs {
 int record_error(int code, const char* msg);
 
 // Launchers (dpg_kernels.hip). Each returns the hipError_t of its launch.
-hipError_t launch_gen_p(const GenPArgs& a, int n_blocks, bool bf16_out,
+// first[i] = L[i].block0 for the n layers of a table, INT32_MAX after them
+template <class Layer>
+inline void index_layers(int32_t (&first)[kMaxLayers], const Layer (&L)[kMaxLayers], int n) {
+  for (int i = 0; i < kMaxLayers; ++i) first[i] = i < n ? L[i].block0 : INT32_MAX;
+}
+
+hipError_t launch_gen_p(GenPArgs a, int n_blocks, bool bf16_out,
                         hipStream_t s);
-hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s);
-hipError_t launch_xsum(const XsumArgs& a, int n_blocks, bool bf16_out,
+hipError_t launch_proj(ProjArgs a, bool bf16_in, bool vec, hipStream_t s);
+hipError_t launch_xsum(XsumArgs a, int n_blocks, bool bf16_out,
                        hipStream_t s);
-hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
+hipError_t launch_samp_norm(SampArgs a, bool bf16_in, bool pair,
                             hipStream_t s);
-hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
+hipError_t launch_samp_sum(SampArgs a, bool bf16_in, bool pair,
                            hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, int B, hipStream_t s);
-hipError_t launch_fin(const FinArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_fin(FinArgs a, int n_blocks, hipStream_t s);
 // fin followed, per element, by the Adam update (m, v in place, U written
 // in bf16 when bf16_out, else fp32)
-hipError_t launch_fin_adam(const FinArgs& a, int n_blocks, bool bf16_out, hipStream_t s);
+hipError_t launch_fin_adam(FinArgs a, int n_blocks, bool bf16_out, hipStream_t s);
 hipError_t launch_norm_acc(const NormAccArgs& a, hipStream_t s);
 hipError_t launch_clip(const ClipArgs& a, hipStream_t s);
-hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
+hipError_t launch_prep(PrepArgs a, int n_blocks, bool bf16_out,
                        hipStream_t s);
-hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s);
+hipError_t launch_back(BackArgs a, bool bf16_in, bool pair, hipStream_t s);
 hipError_t launch_philox_normals(uint32_t k0, uint32_t k1, uint32_t layer_id,
                                  uint32_t step_word, uint32_t tag,
                                  uint32_t start, uint32_t n, float* z_out,

@@ -32,11 +32,19 @@ template <typename T> struct Vec4;
 template <> struct Vec4<bf16> { typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
 
-template <class L>
-__device__ __forceinline__ int find_layer(const L* layers, int n, int b) {
+// The layer of block b among n: the last one whose first block is <= b
+// (first blocks are non-decreasing, the unused entries INT32_MAX). The array
+// is read with wide scalar loads in flight together (its first 16 entries
+// always, the rest only for launches of more than 16 layers); the selects
+// stay on the scalar unit.
+__device__ __forceinline__ int find_layer(const int32_t (&first)[kMaxLayers], int n, int b) {
   int l = 0;
-  for (int i = 1; i < n; ++i)
-    if (b >= layers[i].block0) l = i;
+#pragma unroll
+  for (int i = 1; i < 16; ++i) l = b >= first[i] ? i : l;
+  if (n > 16) {
+#pragma unroll
+    for (int i = 16; i < kMaxLayers; ++i) l = b >= first[i] ? i : l;
+  }
   return l;
 }
 
@@ -111,7 +119,7 @@ __device__ __forceinline__ void gen_p_thread(const GenPLayer& L, int c, int r,
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gen_p_kernel(const GenPArgs a) {
   const int b = blockIdx.x;
-  const GenPLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
+  const GenPLayer& L = a.L[find_layer(a.first_block, a.n_layers, b)];
   const StreamKey key{a.k0, a.k1, a.step_word, a.tag};
   gen_p_thread<T>(L, (b - L.block0) * kThreads + static_cast<int>(threadIdx.x),
                   a.r, a.scale, key);
@@ -133,7 +141,7 @@ __global__ __launch_bounds__(kThreads * NG, 3 - NG) void proj_kernel(const ProjA
   T* smem = smem_all + grp * Tl::kLdsElems;
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const ProjLayer& L = a.L[find_layer(a.first_block, a.n_layers, lb)];
   const int local = lb - L.block0;
   const int mt = local % L.m_tiles;
   const int rest = local / L.m_tiles;
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   __shared__ __attribute__((aligned(1024))) char smem[(2 + NA) * kTileBytes];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const ProjLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const ProjLayer& L = a.L[find_layer(a.first_block, a.n_layers, lb)];
   const int local = lb - L.block0;
   const int mt = local % L.m_tiles;
   const int rest = local / L.m_tiles;
@@ -533,7 +541,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
 template <typename T>
 __global__ __launch_bounds__(kThreads) void xsum_kernel(const XsumArgs a) {
   const int b = blockIdx.x;
-  const XsumLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
+  const XsumLayer& L = a.L[find_layer(a.first_block, a.n_layers, b)];
   const int BT = a.B * a.T;
   const int per_row = (BT + 3) / 4;
   const int64_t idx = static_cast<int64_t>(b - L.block0) * kThreads + threadIdx.x;
@@ -625,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 2) void samp_kernel(const SampArgs a) {
   __shared__ float s_grp[SUM ? kSumMaxGroup : 1];  // the group's clip factors
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const int li = find_layer(a.L, a.n_layers, lb);
+  const int li = find_layer(a.first_block, a.n_layers, lb);
   const SampLayer& L = a.L[li];
   const int local = lb - L.block0;
   const int mt = local % L.m_tiles;
@@ -733,7 +741,7 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const int li = find_layer(a.L, a.n_layers, lb);
+  const int li = find_layer(a.first_block, a.n_layers, lb);
   const SampLayer& L = a.L[li];
   const int local = lb - L.block0;
   const int mt = local % L.m_tiles;
@@ -846,7 +854,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   float* s_grp = reinterpret_cast<float*>(smem + 2 * kStageBytes);
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const int li = find_layer(a.L, a.n_layers, lb);
+  const int li = find_layer(a.first_block, a.n_layers, lb);
   const SampLayer& L = a.L[li];
   const int local = lb - L.block0;
   const int mt = local % L.m_tiles;
@@ -1107,7 +1115,7 @@ __device__ __forceinline__ float adam_dir(const H& a, float g, float& m, float& 
 template <typename T, bool ADAM>
 __global__ __launch_bounds__(kThreads) void fin_kernel(const FinArgs a) {
   const int b = blockIdx.x;
-  const FinLayer& L = a.L[find_layer(a.L, a.n_layers, b)];
+  const FinLayer& L = a.L[find_layer(a.first_block, a.n_layers, b)];
   const int c = (b - L.block0) * kThreads + static_cast<int>(threadIdx.x);
   const int64_t e0 = 4ll * c;
   if (e0 >= L.n_elem) return;
@@ -1215,13 +1223,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepArgs a) {
   const int b = blockIdx.x;
   if (b >= a.adam_blocks) {
     const int bp = b - a.adam_blocks;
-    const GenPLayer& L = a.P[find_layer(a.P, a.n_layers, bp)];
+    const GenPLayer& L = a.P[find_layer(a.first_p, a.n_layers, bp)];
     const StreamKey key{a.k0, a.k1, a.step_word, 0u};
     gen_p_thread<T>(L, (bp - L.block0) * kThreads + static_cast<int>(threadIdx.x),
                     a.r, a.p_scale, key);
     return;
   }
-  const AdamLayer& L = a.A[find_layer(a.A, a.n_layers, b)];
+  const AdamLayer& L = a.A[find_layer(a.first_a, a.n_layers, b)];
   const int c = (b - L.block0) * kThreads + static_cast<int>(threadIdx.x);
   const int64_t e0 = 4ll * c;
   if (e0 >= L.n_elem) return;
@@ -1268,7 +1276,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_kernel(const BackArgs a) {
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const BackLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const BackLayer& L = a.L[find_layer(a.first_block, a.n_layers, lb)];
   const int local = lb - L.block0;
   const int nt = local % L.n_tiles, mt = local / L.n_tiles;
   const int m0 = mt * Tl::BM, n0 = nt * Tl::BN;
@@ -1360,7 +1368,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_res_kernel(const BackArgs a)
   __shared__ __attribute__((aligned(16))) T smem[Tl::kLdsElems];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const BackLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const BackLayer& L = a.L[find_layer(a.first_block, a.n_layers, lb)];
   const int local = lb - L.block0;
   const int c = local % L.n_chunks, mt = local / L.n_chunks;
   const int nt0 = c * a.res_tiles, nt1 = min(L.n_tiles, nt0 + a.res_tiles);
@@ -1475,7 +1483,7 @@ __global__ __launch_bounds__(kThreads, 2) void back_big_kernel(const BackArgs a)
   __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
   const int lb = xcd_logical_block();
   if (lb >= a.n_blocks) return;
-  const BackLayer& L = a.L[find_layer(a.L, a.n_layers, lb)];
+  const BackLayer& L = a.L[find_layer(a.first_block, a.n_layers, lb)];
   // Blocks of a layer: groups of (up to) 8 row tiles; in a group, each run
   // of column tiles for each of its rows, the rows varying fastest. The
   // blocks an XCD runs at once are consecutive, so they cover about 8 rows
@@ -1700,8 +1708,9 @@ static inline unsigned grid8(int n_blocks) {
   return static_cast<unsigned>(round_up(n_blocks, 8));
 }
 
-hipError_t launch_gen_p(const GenPArgs& a, int n_blocks, bool bf16_out,
+hipError_t launch_gen_p(GenPArgs a, int n_blocks, bool bf16_out,
                         hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   const dim3 g(n_blocks), b(kThreads);
   if (bf16_out) hipLaunchKernelGGL(gen_p_kernel<bf16>, g, b, 0, s, a);
   else hipLaunchKernelGGL(gen_p_kernel<float>, g, b, 0, s, a);
@@ -1723,7 +1732,8 @@ static hipError_t launch_proj_ng(const ProjArgs& a, bool bf16_in, bool vec, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s) {
+hipError_t launch_proj(ProjArgs a, bool bf16_in, bool vec, hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   if (a.big) {
     hipLaunchKernelGGL((proj_big_kernel<kBigK>), dim3(grid8(a.n_blocks)),
                        dim3(2 * kThreads), 0, s, a);
@@ -1733,8 +1743,9 @@ hipError_t launch_proj(const ProjArgs& a, bool bf16_in, bool vec, hipStream_t s)
                    : launch_proj_ng<1>(a, bf16_in, vec, s);
 }
 
-hipError_t launch_xsum(const XsumArgs& a, int n_blocks, bool bf16_out,
+hipError_t launch_xsum(XsumArgs a, int n_blocks, bool bf16_out,
                        hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   if (bf16_out) hipLaunchKernelGGL(xsum_kernel<bf16>, dim3(n_blocks), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(xsum_kernel<float>, dim3(n_blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
@@ -1757,8 +1768,9 @@ static hipError_t launch_samp(const SampArgs& a, bool bf16_in, bool pair,
   return hipGetLastError();
 }
 
-hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
+hipError_t launch_samp_norm(SampArgs a, bool bf16_in, bool pair,
                             hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   if (a.big) {
     hipLaunchKernelGGL(samp_big_kernel<false>, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
     return hipGetLastError();
@@ -1776,8 +1788,9 @@ hipError_t launch_samp_norm(const SampArgs& a, bool bf16_in, bool pair,
   return hipGetLastError();
 }
 
-hipError_t launch_samp_sum(const SampArgs& a, bool bf16_in, bool pair,
+hipError_t launch_samp_sum(SampArgs a, bool bf16_in, bool pair,
                            hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   if (a.big) {
     hipLaunchKernelGGL(samp_big_kernel<true>, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
     return hipGetLastError();
@@ -1802,12 +1815,14 @@ hipError_t launch_clip(const ClipArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fin(const FinArgs& a, int n_blocks, hipStream_t s) {
+hipError_t launch_fin(FinArgs a, int n_blocks, hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   hipLaunchKernelGGL((fin_kernel<float, false>), dim3(n_blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fin_adam(const FinArgs& a, int n_blocks, bool bf16_out, hipStream_t s) {
+hipError_t launch_fin_adam(FinArgs a, int n_blocks, bool bf16_out, hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   if (bf16_out)
     hipLaunchKernelGGL((fin_kernel<bf16, true>), dim3(n_blocks), dim3(kThreads), 0, s, a);
   else
@@ -1815,8 +1830,10 @@ hipError_t launch_fin_adam(const FinArgs& a, int n_blocks, bool bf16_out, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
+hipError_t launch_prep(PrepArgs a, int n_blocks, bool bf16_out,
                        hipStream_t s) {
+  index_layers(a.first_a, a.A, a.n_layers);
+  index_layers(a.first_p, a.P, a.n_layers);
   if (bf16_out)
     hipLaunchKernelGGL(prep_kernel<bf16>, dim3(n_blocks), dim3(kThreads), 0, s, a);
   else
@@ -1824,7 +1841,8 @@ hipError_t launch_prep(const PrepArgs& a, int n_blocks, bool bf16_out,
   return hipGetLastError();
 }
 
-hipError_t launch_back(const BackArgs& a, bool bf16_in, bool pair, hipStream_t s) {
+hipError_t launch_back(BackArgs a, bool bf16_in, bool pair, hipStream_t s) {
+  index_layers(a.first_block, a.L, a.n_layers);
   const dim3 g(grid8(a.n_blocks)), b(kThreads);
   if (a.big) {
     hipLaunchKernelGGL(back_big_kernel, g, dim3(kThreads), 0, s, a);

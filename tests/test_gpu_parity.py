@@ -91,9 +91,10 @@ CASES = {
                                          B=5, T=70, r=150, clip_C=0.3,
                                          sigma=0.5),
     "single": W.custom_workload("single", 16, [(8, 8)], B=1, T=1, r=1),
+    # more layers than one launch takes (48): two launches per kernel
     "many_layers": W.custom_workload("many_layers", 17,
-                                     [(24, 16), (16, 24)] * 20, B=2, T=8,
-                                     r=8, layer_ids=list(range(100, 140))),
+                                     [(24, 16), (16, 24)] * 26, B=2, T=8,
+                                     r=8, layer_ids=list(range(100, 152))),
     # bf16 projection on the LDS ring: full 128 x 64 tiles next to ragged
     # ones (r = 160, B*T = 600) and a ragged contraction tail (d_in = 200,
     # 328)
