@@ -463,6 +463,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Context for the HBM fractions: the rate of the runtime's own
+    # device-to-device copy (half reads, half writes, as in the update
+    # kernels' read-modify-write streams), bytes read plus written. Not in
+    # counter runs (--copy-mb), whose calibration takes the last copies.
+    hbm_copy = None
+    if args.copy_mb == 0:
+        n = 512 * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * 4 * n * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        hbm_copy = {"GB/s": round(copy_gbs, 1), "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                    "what": "device-to-device copy of 512 MiB, bytes read plus written"}
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -493,6 +517,7 @@ def main():
         "two_call": two_call,
         "streaming": streaming,
         "rc_norms": rc,
+        "hbm_copy": hbm_copy,
     }
     print(json.dumps(out), flush=True)
 
