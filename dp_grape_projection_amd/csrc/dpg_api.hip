@@ -234,6 +234,17 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
         static_cast<uint64_t>(BT) * layers[l].d_in * 2 >= (1ull << 32) ||
         static_cast<uint64_t>(r) * round_up(layers[l].d_in, 8) * 2 >= (1ull << 32))
       p.big = false;
+  // A launch with fewer large tiles than CUs would split d_in and add the
+  // partials back; the regular tiles, four times as many, fill the chip
+  // without that once they number at least the CUs. This is the case of
+  // per-layer calls (the streaming form) at r = 256 or 512 and B·T in the
+  // thousands; launches of several large layers keep the large tiles.
+  {
+    const int64_t per_launch = std::min<int64_t>(n_layers, kMaxLayers), cus = target / 2;
+    if (p.big && (r / kBigM) * (BT / kBigN) * per_launch < cus &&
+        mt * ceil_div(BT, kTileN) * per_launch >= cus)
+      p.big = false;
+  }
   int64_t big_sps = 0;
   if (p.big) {
     const int64_t tiles = (r / kBigM) * (BT / kBigN), cus = target / 2;
