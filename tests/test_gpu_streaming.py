@@ -50,6 +50,11 @@ CASES = {
     # back-projection
     "big_tiles_bf16": W.custom_workload("s_big_tiles_bf16", 35,
                                         [(256, 512), (512, 256)], B=2, T=256, r=256),
+    # one layer with fewer 256 x 256 projection tiles (64) than CUs but as
+    # many 128 x 128 ones (256): the plan gives the per-layer projection the
+    # regular tiles instead of splitting d_in
+    "regular_tiles_bf16": W.custom_workload("s_regular_tiles_bf16", 36, [(256, 320)],
+                                            B=16, T=512, r=512),
 }
 
 
