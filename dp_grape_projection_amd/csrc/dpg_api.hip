@@ -151,7 +151,7 @@ int step_of(int32_t dtype) { return dtype == DPG_BF16 ? kStepBf16 : kStepF32; }
 
 // Tiling of the two per-sample passes (squared-norm partials, clipped sum).
 struct SampPlan {
-  bool big = false;  // samp_big_kernel: kBigM x kBigN tiles, 8 waves
+  bool big = false;  // samp_big_kernel: kBigM x kBigN tiles, 16 waves
   std::vector<int32_t> m_tiles, n_tiles, slot0;  // per layer; slot0 in tiles
   int32_t n_slots = 0;         // partials per sample: one per (tile, wave)
   int32_t norm_per_block = 1;  // samples per norm block
@@ -220,7 +220,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   const int64_t target = target_blocks(dtype);
   const int64_t steps_per_block = std::max<int64_t>(1, ceil_div(units, target / 2));
   // Large bf16 projections run in 256 x 256 tiles with K steps of 64, one
-  // 8-wave block per CU. The K steps per block minimise an estimate of the
+  // 16-wave block per CU. The K steps per block minimise an estimate of the
   // time in steps (per launch, below) plus the split partials.
   // (its epilogue stores use 32-bit offsets: all of Xt, and 256 rows of a
   // split partial)
@@ -406,7 +406,7 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   q.fuse_scale = q.per_group <= kFuseMaxGroup && q.n_slots <= kFuseMaxSlots;
 
   // Large per-sample passes (bf16; r, d_out whole 256 x 256 tiles; T whole
-  // K steps): one 8-wave block per CU, launched kMaxLayers layers at a time.
+  // K steps): one 16-wave block per CU, launched kMaxLayers layers at a time.
   // The norm run and the sum group minimise the same estimates, summed over
   // the launches, with the rounds of resident blocks counted in K steps
   // (plus two per block for the pipeline's fill).
@@ -428,8 +428,8 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
       const int32_t nt = static_cast<int32_t>(layers[l].d_out / kBigN);
       b.m_tiles.push_back(mtb);
       b.n_tiles.push_back(nt);
-      b.slot0.push_back(b.n_slots / 8);
-      b.n_slots += 8 * mtb * nt;  // one partial per wave
+      b.slot0.push_back(b.n_slots / 16);
+      b.n_slots += 16 * mtb * nt;  // one partial per wave
       if (l % kMaxLayers == 0) chunk_tiles.push_back(0);
       chunk_tiles.back() += static_cast<int64_t>(mtb) * nt;
     }

@@ -26,7 +26,7 @@ constexpr int kBackN = 64;  // back-projection: 128 x 64 output tiles
 constexpr int kSumBatch = 8;
 // Large projections (bf16, r and B*T whole multiples of 256, d_in of 64):
 // 256 x 256 output tiles, K steps of 64, operands copied to LDS by direct
-// loads in two stages, 8 waves per block.
+// loads (two stages of P, three of A), 16 waves per block.
 constexpr int kBigM = 256, kBigN = 256, kBigK = 64;
 constexpr int kSampBigK = 64;  // K step (over t) of the large norm and sum kernel
 // Large back-projection: 256 (d_in) x 128 (d_out) tiles, K steps of 32 over r,
@@ -141,7 +141,7 @@ struct SampArgs {
   float* norms_out;     // sum mode, fused: [B] or null (written by layer 0's
                         // first tile of each group)
   int32_t big;          // samp_big_kernel: kBigM x kBigN tiles, steps of
-                        // kSampBigK, 8 partial slots per (sample, tile)
+                        // kSampBigK, 16 partial slots per (sample, tile)
 };
 
 // ---- n_i, s_i from the partials

@@ -286,8 +286,11 @@ __device__ __forceinline__ void load_batch(f32x4 (&buf)[kSumBatch], const float*
 // 16-byte LDS read serves 16 lanes (256 bytes) at a time, and rows of 128
 // bytes put even rows in one half of the 64 banks and odd rows in the other,
 // so chunk c of row R goes to slot c ^ (R / 2 mod 8), which gives the 16
-// consecutive rows of a lane group 16 different bank ranges. Waves are 2 (j)
-// x 4 (n); each computes 128 x 64 with 32x32x16 MFMAs.
+// consecutive rows of a lane group 16 different bank ranges. 16 waves, 4
+// (j) x 4 (n), four on each SIMD; each computes 64 x 64 with 32x32x16
+// MFMAs. (8 waves of 128 x 64 read a third fewer fragments a step, but two
+// waves on a SIMD hide less LDS and barrier latency: at dec24 the 16-wave
+// form is 5 % faster, at long1 3 % slower.)
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
@@ -335,23 +338,23 @@ __device__ __forceinline__ float lds_read_f32(const float* __restrict__ p) { ret
 // sub-steps of 16 and across steps. In each sub-step the wave issues one
 // MFMA (its operand wait then covers only the reads issued during the
 // previous sub-step), then the next sub-step's fragment reads, then the other
-// seven MFMAs, so LDS latency hides behind matrix-core work. In the last
-// sub-step of step s, after four MFMAs, every wave has read all of step s:
+// three MFMAs, so LDS latency hides behind matrix-core work. In the last
+// sub-step of step s, after two MFMAs, every wave has read all of step s:
 // it waits for its copies of step s + 1, meets the others at the barrier,
 // refills P's stage of step s with step s + 2 and A's with step s + 3, and
-// reads the first fragments of step s + 1 while the remaining four MFMAs
+// reads the first fragments of step s + 1 while the remaining two MFMAs
 // run.
 template <int BK>
-__global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArgs a) {
+__global__ __launch_bounds__(4 * kThreads, 1) void proj_big_kernel(const ProjArgs a) {
   constexpr int kRowBytes = BK * 2;
   constexpr int CH = kRowBytes / 16;                 // chunks per row
   constexpr int kRowsPerCopy = 1024 / kRowBytes;      // rows per 1 KiB copy
   constexpr int kCopiesPerTile = kBigM / kRowsPerCopy;
-  constexpr int kCopiesPerWave = 2 * kCopiesPerTile / 8;  // per step
+  constexpr int kCopiesPerWave = 2 * kCopiesPerTile / 16;  // per step
   constexpr int kTileBytes = kBigM * kRowBytes;
   constexpr int KK = BK / 16;                         // sub-steps per step
   static_assert(kBigM == kBigN && BK % 16 == 0 && (CH & (CH - 1)) == 0 && KK >= 2, "tile shape");
-  static_assert(kCopiesPerWave * 8 == 2 * kCopiesPerTile, "copies per wave");
+  static_assert(kCopiesPerWave * 16 == 2 * kCopiesPerTile, "copies per wave");
   // Three stages of the A tile (the operand streamed from HBM, whose copies
   // run two steps ahead of their use) and two of P (L2-resident): 160 KiB.
   constexpr int NA = 3;
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   const int j0 = mt * kBigM, n0 = nt * kBigN;
   const int BT = a.B * a.T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int n_steps_all = L.d_in / BK;
   const int s_begin = split * L.steps_per_split;
   const int s_end = min(n_steps_all, s_begin + L.steps_per_split);
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   auto slot = [](int R, int c) { return c ^ ((R >> 1) & (CH - 1)); };
 
   // Copies K step `step` into stage `stage`: copy q of wave w fills row
-  // block g = q * 8 + w (P blocks first, then A blocks); lane l writes slot
+  // block g = q * 16 + w (P blocks first, then A blocks); lane l writes slot
   // l % CH of row l / CH of the block, loading the chunk that the swizzle
   // puts there (it is an involution). A block's index has the parity of w,
   // so each lane's offset within its block is the same for every copy of a
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
     const uint32_t kb = static_cast<uint32_t>(s_begin + step) * kRowBytes;
 #pragma unroll
     for (int q = 0; q < kCopiesA; ++q) {
-      const int gi = q * 8 + wave;
+      const int gi = q * 16 + wave;
       const uint32_t row0 = static_cast<uint32_t>(j0 + gi * kRowsPerCopy);
       copy_to_lds(rsP, voffP, row0 * p_rb + kb, sb + gi * 1024);
     }
@@ -408,13 +411,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
     const uint32_t kb = static_cast<uint32_t>(s_begin + step) * kRowBytes;
 #pragma unroll
     for (int q = 0; q < kCopiesA; ++q) {
-      const int gi = q * 8 + wave;
+      const int gi = q * 16 + wave;
       const uint32_t row0 = static_cast<uint32_t>(n0 + gi * kRowsPerCopy);
       copy_to_lds(rsA, voffA, row0 * a_rb + kb, sb + gi * 1024);
     }
   };
 
-  Acc<4, 2> acc;
+  Acc<2, 2> acc;
   acc.zero();
   const int r32 = lane & 31, kh = lane >> 5;
   // fragments of sub-step kk of the step in stage `stage`: this lane's
@@ -424,8 +427,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
     const char* sA = smem + (2 + step % NA) * kTileBytes;
     const int c = 2 * kk + kh;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int j = 128 * wm + 32 * mb + r32;
+    for (int mb = 0; mb < 2; ++mb) {
+      const int j = 64 * wm + 32 * mb + r32;
       af[mb] = lds_read_b128(sP + j * kRowBytes + slot(j, c) * 16);
     }
 #pragma unroll
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   // MFMAs q0 .. q1 - 1 of a sub-step's eight (q = 2 mb + nb)
   auto mma = [&](const bf16x8* af, const bf16x8* bfr, int q0, int q1) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < 4; ++q)
       if (q >= q0 && q < q1)
         acc.v[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             af[q >> 1], bfr[q & 1], acc.v[q >> 1][q & 1], 0, 0, 0);
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
   // step s + NA. So before that barrier, step s + 1's copies are complete
   // once at most the A copies of step s + 2 (NA = 3) are still in flight:
   // loads return in order.
-  bf16x8 fa[2][4], fb[2][2];
+  bf16x8 fa[2][2], fb[2][2];
   int a_stage = 0;  // the A stage of step s: s mod NA
   if (n_steps > 0) {
     issue_p(0, 0);
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
-      const int first = kk + 1 < KK ? 1 : 4;
+      const int first = kk + 1 < KK ? 1 : 2;
       __builtin_amdgcn_sched_barrier(0);
       mma(fa[cur], fb[cur], 0, first);
       __builtin_amdgcn_sched_barrier(0);
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
         read_frags(s + 1, 0, fa[nxt], fb[nxt]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      mma(fa[cur], fb[cur], first, 8);
+      mma(fa[cur], fb[cur], first, 4);
       __builtin_amdgcn_sched_barrier(0);
     }
     a_stage = a_stage + 1 == NA ? 0 : a_stage + 1;
@@ -500,10 +503,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
     for (int nb = 0; nb < 2; ++nb) {
       const int n = n0 + 64 * wn + 32 * nb + r32;
       const int bi = n / a.T, t = n - bi * a.T;
-      const uint32_t lo = (static_cast<uint32_t>(bi * a.r + j0 + 128 * wm + 4 * kh)) * row2 +
+      const uint32_t lo = (static_cast<uint32_t>(bi * a.r + j0 + 64 * wm + 4 * kh)) * row2 +
                           static_cast<uint32_t>(t) * 2u;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const bf16 v = from_float<bf16>(acc.v[mb][nb][i]);
@@ -516,14 +519,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void proj_big_kernel(const ProjArg
     }
   } else {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(
-        L.part + (static_cast<int64_t>(split) * a.r + j0 + 128 * wm) * BT);
+        L.part + (static_cast<int64_t>(split) * a.r + j0 + 64 * wm) * BT);
     const uint32_t row4 = static_cast<uint32_t>(BT) * 4u;
     const uint32_t lo = static_cast<uint32_t>(4 * kh) * row4 +
                         static_cast<uint32_t>(n0 + 64 * wn + r32) * 4u;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float v = acc.v[mb][nb][i];
@@ -788,7 +791,7 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
 
 // Norm and sum passes in 256 x 256 tiles (rows j of Xt over r, columns n of
 // dY over d_out) for bf16 with r and d_out whole tiles and T a multiple of
-// kSampBigK: one 8-wave block per CU, K steps over t, two stages of direct
+// kSampBigK: one 16-wave block per CU, K steps over t, two stages of direct
 // global-to-LDS copies, the step index running over (sample, t) so that the
 // copies flow on across the samples of a block. Xt tiles (t contiguous) sit
 // in LDS as the projection's P tiles do. dY tiles stay row-major [t][n], 512
@@ -796,9 +799,10 @@ __global__ __launch_bounds__(kThreads, 2) void norm_res_kernel(const SampArgs a)
 // operand is read from them with the transposing LDS read: in each group of
 // 16 lanes, lane q gives four consecutive n of row t0 + q / 4, and lane j
 // receives element j % 4 of what lanes j / 4, 4 + j / 4, 8 + j / 4 and
-// 12 + j / 4 gave, i.e. four consecutive t of one column. Waves are 2 (j) x 4
-// (n), each computing 128 x 64. Norm mode writes one squared-norm partial per
-// (sample, tile, wave); sum mode keeps the running clipped sum of samp_kernel.
+// 12 + j / 4 gave, i.e. four consecutive t of one column. Waves are 4 (j) x 4
+// (n), each computing 64 x 64 (as in the projection). Norm mode writes one
+// squared-norm partial per (sample, tile, wave), 16 per (sample, tile); sum
+// mode keeps the running clipped sum of samp_kernel.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -836,16 +840,16 @@ __device__ __forceinline__ bf16x8 frag_kmajor(const char* tile, int k0, int c0, 
 }
 
 template <bool SUM>
-__global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArgs a) {
+__global__ __launch_bounds__(4 * kThreads, 1) void samp_big_kernel(const SampArgs a) {
   constexpr int BK = kSampBigK;
   constexpr int kRowA = BK * 2, CHA = kRowA / 16;        // Xt tile rows
   constexpr int kRowB = kBigN * 2, CHB = kRowB / 16;     // dY tile rows
   constexpr int kTileBytes = kBigM * kRowA;
   constexpr int kBlocksA = kTileBytes / 1024;            // 1 KiB copies per tile
-  constexpr int kCopies = 2 * kBlocksA / 8;              // per wave and step
+  constexpr int kCopies = 2 * kBlocksA / 16;             // per wave and step
   constexpr int kStageBytes = 2 * kTileBytes;
   static_assert(kTileBytes == BK * kRowB && kBigM == kBigN, "equal square tiles");
-  static_assert(kCopies * 8 == 2 * kBlocksA && kCopies % 2 == 0, "copies per wave");
+  static_assert(kCopies * 16 == 2 * kBlocksA && kCopies % 2 == 0, "copies per wave");
   static_assert(CHA == 8 && CHB == 32, "swizzles assume 128- and 512-byte rows");
   // the stages, then (sum mode) the group's clip factors: one LDS object
   // (with the factors in an array of their own the compiler made the main
@@ -863,7 +867,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   const int g = rest / L.n_tiles;  // run (norm) or group (sum) of samples
   const int j0 = mt * kBigM, n0 = nt * kBigN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int i_begin = g * a.per_block;
   const int i_end = min(a.B, i_begin + a.per_block);
   const int kc = a.T / BK;  // steps per sample
@@ -872,7 +876,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   auto slot_a = [](int R, int c) { return c ^ ((R >> 1) & (CHA - 1)); };
 
   // Copies step `step` into stage `stage`: copy q of wave w fills 1 KiB
-  // block q * 8 + w (Xt blocks of 8 rows first, then dY blocks of 2 rows);
+  // block q * 16 + w (Xt blocks of 8 rows first, then dY blocks of 2 rows);
   // lane l writes the block's 16-byte slot l, loading the chunk that the
   // swizzle puts there (the swizzles are involutions). A block's index has
   // the parity of w, so each lane's offset within its block is fixed for a
@@ -892,7 +896,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
     const uint32_t by = static_cast<uint32_t>(i * a.T + k0) * yr + static_cast<uint32_t>(n0) * 2u;
 #pragma unroll
     for (int q = 0; q < kCopies; ++q) {
-      const int blk = q * 8 + wave;
+      const int blk = q * 16 + wave;
       if (q < kCopies / 2)
         copy_to_lds(rsX, voffX, bx + static_cast<uint32_t>(blk * (1024 / kRowA)) * xr, sb + blk * 1024);
       else
@@ -903,12 +907,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
 
   if (SUM) {
     if (!a.fuse_scale) {
-      for (int q = tid; q < i_end - i_begin; q += 2 * kThreads) s_grp[q] = a.scales[i_begin + q];
+      for (int q = tid; q < i_end - i_begin; q += 4 * kThreads) s_grp[q] = a.scales[i_begin + q];
     } else {
       // per-sample global norm and clip factor of this group, summed in the
-      // same order as samp_kernel (wave w takes samples w, w + 8, ...)
+      // same order as samp_kernel (wave w takes samples w, w + 16, ...)
       const int jn = (a.n_slots + 63) >> 6;
-      for (int q = wave; q < i_end - i_begin; q += 8) {
+      for (int q = wave; q < i_end - i_begin; q += 16) {
         const float* p = a.norm_part + static_cast<int64_t>(i_begin + q) * a.n_slots;
         float v[kFuseMaxSlots / 64];
 #pragma unroll
@@ -928,7 +932,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
     __syncthreads();
   }
 
-  Acc<4, 2> acc;
+  Acc<2, 2> acc;
   acc.zero();
   float c = 0.0f;  // sum mode: factor the accumulator is expressed in
   bool on = true;  // sum mode: the current sample is accumulated
@@ -941,8 +945,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
     const char* sY = sX + kTileBytes;
     const int cx = 2 * kk + kh;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int j = 128 * wm + 32 * mb + r32;
+    for (int mb = 0; mb < 2; ++mb) {
+      const int j = 64 * wm + 32 * mb + r32;
       af[mb] = lds_read_b128(sX + j * kRowA + slot_a(j, cx) * 16);
     }
 #pragma unroll
@@ -950,7 +954,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   };
   auto mma = [&](const bf16x8* af, const bf16x8* bfr, int q0, int q1) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < 4; ++q)
       if (q >= q0 && q < q1)
         acc.v[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             af[q >> 1], bfr[q & 1], acc.v[q >> 1][q & 1], 0, 0, 0);
@@ -959,7 +963,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
   // sub-steps and across steps, the stage wait and barrier in the middle of
   // the last sub-step, the refill into the stage just read
   constexpr int KK = BK / 16;
-  bf16x8 fa[2][4], fb[2][2];
+  bf16x8 fa[2][2], fb[2][2];
   if (n_steps > 0) {
     issue(0, 0);
     wait_vm(0);
@@ -984,7 +988,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int cur = kk & 1, nxt = cur ^ 1;
-        const int first = kk + 1 < KK ? 1 : 4;
+        const int first = kk + 1 < KK ? 1 : 2;
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (M) mma(fa[cur], fb[cur], 0, first);
         __builtin_amdgcn_sched_barrier(0);
@@ -998,7 +1002,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
           read_frags((s + 1) & 1, 0, fa[nxt], fb[nxt]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (M) mma(fa[cur], fb[cur], first, 8);
+        if constexpr (M) mma(fa[cur], fb[cur], first, 4);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -1009,18 +1013,18 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
       const float t = wave_sum(acc.sum_sq());
       if (lane == 0)
         a.norm_part[static_cast<int64_t>(i) * a.n_slots +
-                    8 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
+                    16 * (L.slot0 + nt * L.m_tiles + mt) + wave] = t;
       if (L.ghat) {
         // the sample's product tile into ghat [B][r][d_out], through a buffer
-        // resource on the wave's 128 rows (lane: column n0 + 64 wn + 32 nb +
+        // resource on the wave's 64 rows (lane: column n0 + 64 wn + 32 nb +
         // r32; register q: row 32 mb + 8 (q / 4) + 4 kh + q % 4)
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(
-            L.ghat + (static_cast<int64_t>(i) * a.r + j0 + 128 * wm) * L.d_out);
+            L.ghat + (static_cast<int64_t>(i) * a.r + j0 + 64 * wm) * L.d_out);
         const uint32_t row4 = static_cast<uint32_t>(L.d_out) * 4u;
         const uint32_t lo = static_cast<uint32_t>(4 * kh) * row4 +
                             static_cast<uint32_t>(n0 + 64 * wn + r32) * 4u;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -1041,19 +1045,19 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
 
   if (SUM) {
     // the group's partial [r][d_out], through a buffer resource on the
-    // wave's 128 rows (lane: column n0 + 64 wn + 32 nb + r32; register q:
+    // wave's 64 rows (lane: column n0 + 64 wn + 32 nb + r32; register q:
     // row 32 mb + 8 (q / 4) + 4 kh + q % 4). One lane offset and uniform
     // row offsets: per-element 64-bit addresses here raised the register
     // pressure of the whole kernel enough that the main loop's fragment
     // reads waited for the step's copies.
     acc.scale(c);
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(
-        L.part + (static_cast<int64_t>(g) * a.r + j0 + 128 * wm) * L.d_out);
+        L.part + (static_cast<int64_t>(g) * a.r + j0 + 64 * wm) * L.d_out);
     const uint32_t row4 = static_cast<uint32_t>(L.d_out) * 4u;
     const uint32_t lo = static_cast<uint32_t>(4 * kh) * row4 +
                         static_cast<uint32_t>(n0 + 64 * wn + r32) * 4u;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -1073,7 +1077,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void samp_big_kernel(const SampArg
 __global__ __launch_bounds__(kScaleThreads) void scale_kernel(const ScaleArgs a) {
   // one block per sample; thread t adds the 16-byte groups t, t + 1024,
   // ... of the sample's slots (n_slots is a multiple of 4: every tiling
-  // writes 4 or 8 partials per tile), then a fixed-order reduction
+  // writes 4 or 16 partials per tile), then a fixed-order reduction
   __shared__ float red[kScaleThreads / 64];
   const int i = blockIdx.x, tid = threadIdx.x;
   const float* p = a.norm_part + static_cast<int64_t>(i) * a.n_slots;
@@ -1736,7 +1740,7 @@ hipError_t launch_proj(ProjArgs a, bool bf16_in, bool vec, hipStream_t s) {
   index_layers(a.first_block, a.L, a.n_layers);
   if (a.big) {
     hipLaunchKernelGGL((proj_big_kernel<kBigK>), dim3(grid8(a.n_blocks)),
-                       dim3(2 * kThreads), 0, s, a);
+                       dim3(4 * kThreads), 0, s, a);
     return hipGetLastError();
   }
   return a.groups2 ? launch_proj_ng<2>(a, bf16_in, vec, s)
@@ -1772,7 +1776,7 @@ hipError_t launch_samp_norm(SampArgs a, bool bf16_in, bool pair,
                             hipStream_t s) {
   index_layers(a.first_block, a.L, a.n_layers);
   if (a.big) {
-    hipLaunchKernelGGL(samp_big_kernel<false>, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
+    hipLaunchKernelGGL(samp_big_kernel<false>, dim3(grid8(a.n_blocks)), dim3(4 * kThreads), 0, s, a);
     return hipGetLastError();
   }
   if (a.res_tiles == 0) return launch_samp<kTileN, false>(a, bf16_in, pair, s);
@@ -1792,7 +1796,7 @@ hipError_t launch_samp_sum(SampArgs a, bool bf16_in, bool pair,
                            hipStream_t s) {
   index_layers(a.first_block, a.L, a.n_layers);
   if (a.big) {
-    hipLaunchKernelGGL(samp_big_kernel<true>, dim3(grid8(a.n_blocks)), dim3(2 * kThreads), 0, s, a);
+    hipLaunchKernelGGL(samp_big_kernel<true>, dim3(grid8(a.n_blocks)), dim3(4 * kThreads), 0, s, a);
     return hipGetLastError();
   }
   return launch_samp<kTileN, true>(a, bf16_in, pair, s);
