@@ -223,7 +223,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs the DP-GRAPE step on one GPU; --gpus {args.gpus} "
-              "is not supported by this build (no multi-GPU path).",
+              "is not supported (the library has no multi-GPU path).",
               file=sys.stderr)
         sys.exit(2)
     for k in ("RANK", "WORLD_SIZE"):
