@@ -276,8 +276,13 @@ def test_mixed_clipping(name):
     _check_project(wl, host, orc, sigma=0.0, C=C, tag=" mixed")
 
 
-def test_deterministic_bitwise():
-    wl = CASES["multi_tile_bf16"]
+@pytest.mark.parametrize("name", ["multi_tile_bf16", "big_bf16", "samp_big_r512_bf16",
+                                  "back_big_bf16"])
+def test_deterministic_bitwise(name):
+    """Two runs of the same step give the same bits: the regular tiles, the
+    large projection, the large per-sample kernels (r = 512) and the large
+    back-projection."""
+    wl = CASES[name]
     host, _, state = make_case(wl)
     G1, n1 = run_project(wl, host)
     G2, n2 = run_project(wl, host)
