@@ -864,11 +864,10 @@ int project_impl(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
     }
   }
 
-  // the large per-sample kernel copies dY rows with 16-byte transfers; the
-  // streaming form (which also stores each sample's product) takes the
-  // regular one
+  // the large per-sample kernel copies dY rows with 16-byte transfers (in
+  // the streaming form it also stores each sample's product tile)
   const bool hat_sum = p.hat_sum && !layer_mode && !rc;
-  bool samp_big = p.has_samp_big && !layer_mode;
+  bool samp_big = p.has_samp_big;
   for (int l = 0; l < n_layers; ++l)
     if (!aligned(layers[l].dY, 16)) samp_big = false;
   const SampPlan& sp = samp_big ? p.samp_big : p.samp;
