@@ -238,11 +238,15 @@ ProjPlan plan_proj(const dpg_layer_grad* layers, int32_t n_layers, int64_t B,
   // partials back; the regular tiles, four times as many, fill the chip
   // without that once they number at least the CUs. This is the case of
   // per-layer calls (the streaming form) at r = 256 or 512 and B·T in the
-  // thousands; launches of several large layers keep the large tiles.
+  // thousands, unless the layers are long enough in d_in (more than 64
+  // large K steps) for the split partials to be a small part of the work;
+  // launches of several large layers keep the large tiles.
   {
     const int64_t per_launch = std::min<int64_t>(n_layers, kMaxLayers), cus = target / 2;
+    int64_t max_steps = 0;
+    for (int l = 0; l < n_layers; ++l) max_steps = std::max<int64_t>(max_steps, layers[l].d_in / kBigK);
     if (p.big && (r / kBigM) * (BT / kBigN) * per_launch < cus &&
-        mt * ceil_div(BT, kTileN) * per_launch >= cus)
+        mt * ceil_div(BT, kTileN) * per_launch >= cus && max_steps <= 64)
       p.big = false;
   }
   int64_t big_sps = 0;
